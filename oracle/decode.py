@@ -1,0 +1,174 @@
+"""Oracle decode loop for the three modes (test infrastructure only).
+
+State (reading R4): the committed tokens x[0..L) and a cache holding causal
+K/V for positions [0, kv_len).  Tokens x[kv_len..L) are *pending*: committed
+but not yet run through the model.  A forward's rows are the pending tokens as
+clean causal rows, optionally followed by a block of rows at [L, L + nb).
+
+* AR [Notes §5.1; Blog, "纯自回归 ar_mode=true"]: one forward over the pending
+  rows; the greedy token of the last row is the next token.
+* Diffusion [Notes §5.2; Blog, "扩散模式 FastDiffuser"]: a block of B [MASK]
+  rows predicting their own positions (reading R2), re-run until every
+  position is committed by the threshold rule (readings R5, R6, R8).
+* Self-speculation [Notes §5.3; Digest, Method; Blog, "自推测 LinearSpec"]: a
+  draft forward (pending rows + k [MASK] rows, LoRA on the mask rows only)
+  gives the AR token g0 and k drafts; a causal verify forward over the drafts
+  gives g1..gk; the longest matching prefix a is accepted and g0..ga committed
+  (1..k+1 tokens), the K/V of the k - a rejected rows rolled back.
+
+Every step counts its executed forwards; TPF = committed tokens / forwards,
+the draft and verify forwards counted separately (reading R17).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+from .model import KVCache, OracleModel, Row, forward
+from .sampler import accept_length, commit_set, vocab_reduce
+
+MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC = 0, 1, 2
+
+
+@dataclasses.dataclass
+class ForwardRecord:
+    rows: List[Row]
+    lora: bool
+    logits: Optional[np.ndarray]
+
+
+class OracleSession:
+    def __init__(self, model: OracleModel, max_ctx: int, keep_logits: bool = False,
+                 prefill_chunk: int = 64):
+        self.model = model
+        self.cache = KVCache(model.shape, max_ctx)
+        self.tokens: List[int] = []
+        self.kv_len = 0
+        self.forwards = 0
+        self.rounds = 0
+        self.accepts: List[int] = []
+        self.keep_logits = keep_logits
+        self.prefill_chunk = prefill_chunk
+        self.records: List[ForwardRecord] = []
+
+    # -- basic pieces ---------------------------------------------------
+    @property
+    def L(self) -> int:
+        return len(self.tokens)
+
+    def run(self, rows: List[Row], lora: bool = False, count: bool = True) -> np.ndarray:
+        logits = forward(self.model, self.cache, rows, lora_enabled=lora)
+        if count:
+            self.forwards += 1
+        self.records.append(ForwardRecord(rows, lora, logits if self.keep_logits else None))
+        return logits
+
+    def clean_rows(self) -> List[Row]:
+        """The pending tokens as clean causal rows (hi = pos + 1)."""
+        return [Row(self.tokens[p], p, p + 1) for p in range(self.kv_len, self.L)]
+
+    def prefill(self, prompt) -> None:
+        """Run x[0..P-1) causally into the cache; x[P-1] stays pending (R15).
+        Not counted as decode forwards."""
+        toks = [int(t) for t in prompt]
+        if not toks:
+            raise ValueError("empty prompt")
+        self.tokens = toks
+        self.kv_len = 0
+        n = len(toks) - 1
+        for s in range(0, n, self.prefill_chunk):
+            e = min(n, s + self.prefill_chunk)
+            self.run([Row(toks[p], p, p + 1) for p in range(s, e)], count=False)
+        self.kv_len = n
+
+    def kv_append(self, n: int) -> None:
+        if self.kv_len + n > self.L:
+            raise ValueError("append beyond committed tokens")
+        self.kv_len += n
+
+    def kv_rollback(self, n: int) -> None:
+        if n < 0 or n > self.kv_len:
+            raise ValueError("bad rollback")
+        self.kv_len -= n
+
+    # -- the three modes -------------------------------------------------
+    def ar_step(self) -> List[int]:
+        rows = self.clean_rows()
+        logits = self.run(rows)
+        g, _ = vocab_reduce(logits[-1])
+        self.kv_append(len(rows))
+        self.tokens.append(g)
+        self.rounds += 1
+        return [g]
+
+    def diffusion_block(self, block: int, threshold: float) -> List[int]:
+        mask = self.model.shape.mask_id
+        L = self.L
+        y = [mask] * block
+        done = [False] * block
+        first = True
+        while not all(done):
+            clean = self.clean_rows() if first else []
+            rows = clean + [Row(y[i], L + i, L + block) for i in range(block)]
+            logits = self.run(rows)
+            if first:
+                self.kv_append(len(clean))
+                first = False
+            tok = [0] * block
+            conf = [0.0] * block
+            for i in range(block):
+                if not done[i]:
+                    tok[i], conf[i] = vocab_reduce(logits[len(clean) + i])
+            for i in commit_set(conf, [not d for d in done], threshold):
+                y[i] = tok[i]
+                done[i] = True
+        self.tokens.extend(y)
+        self.rounds += 1
+        return y
+
+    def draft(self, k: int, lora: bool = False):
+        """The draft forward: returns (g0, drafts) and appends the pending rows."""
+        mask = self.model.shape.mask_id
+        L = self.L
+        clean = self.clean_rows()
+        rows = clean + [Row(mask, L + i, L + k, lora=True) for i in range(k)]
+        logits = self.run(rows, lora=lora)
+        g0, _ = vocab_reduce(logits[len(clean) - 1])
+        d = [vocab_reduce(logits[len(clean) + i])[0] for i in range(k)]
+        self.kv_append(len(clean))
+        return g0, d
+
+    def verify(self, d: List[int]) -> List[int]:
+        """The verify forward over the drafts as causal rows: returns g1..gk."""
+        L = self.L
+        rows = [Row(d[i], L + i, L + i + 1) for i in range(len(d))]
+        logits = self.run(rows)
+        return [vocab_reduce(logits[i])[0] for i in range(len(d))]
+
+    def selfspec_round(self, k: int, lora: bool = False) -> List[int]:
+        g0, d = self.draft(k, lora)
+        g = [g0] + self.verify(d)
+        a = accept_length(d, g)
+        L = self.L
+        self.tokens.extend(g[: a + 1])
+        self.kv_len = L + a          # append the k verify rows, roll back k - a
+        self.rounds += 1
+        self.accepts.append(a)
+        return g[: a + 1]
+
+    def generate(self, mode: int, n_new: int, block: int = 32, threshold: float = 0.9,
+                 lora: bool = False) -> List[int]:
+        """Generate exactly ``n_new`` tokens (no EOS, overshoot truncated: R13)."""
+        out: List[int] = []
+        while len(out) < n_new:
+            if mode == MODE_AR:
+                out += self.ar_step()
+            elif mode == MODE_DIFFUSION:
+                out += self.diffusion_block(block, threshold)
+            elif mode == MODE_SELFSPEC:
+                out += self.selfspec_round(block, lora)
+            else:
+                raise ValueError(f"bad mode {mode}")
+        return out[:n_new]

@@ -1,0 +1,90 @@
+"""ctypes declarations of libtrimode.so (include/trimode.h).  Marshalling only."""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtrimode.so")
+
+TRI_OK, TRI_EINVAL, TRI_ECAPACITY, TRI_ESTATE, TRI_EHIP, TRI_ENUMERIC = 0, -1, -2, -3, -4, -5
+TRI_AR, TRI_DIFFUSION, TRI_SELFSPEC = 0, 1, 2
+TRI_F32, TRI_BF16 = 0, 1
+
+_ERR_NAMES = {TRI_EINVAL: "TRI_EINVAL", TRI_ECAPACITY: "TRI_ECAPACITY", TRI_ESTATE: "TRI_ESTATE",
+              TRI_EHIP: "TRI_EHIP", TRI_ENUMERIC: "TRI_ENUMERIC"}
+
+
+class TriError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{_ERR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ffn", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("lora_rank", ctypes.c_int32)]
+
+
+class SeqStats(ctypes.Structure):
+    _fields_ = [("n_committed", ctypes.c_int32), ("n_forwards", ctypes.c_int32),
+                ("accept_len", ctypes.c_int32), ("n_flags", ctypes.c_int32)]
+
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+F = ctypes.c_float
+SZ = ctypes.c_size_t
+IP = ctypes.POINTER(ctypes.c_int32)
+FP = ctypes.POINTER(ctypes.c_float)
+
+# name -> (restype, argtypes); every exported symbol of the header
+SIGNATURES = {
+    "tri_last_error": (ctypes.c_char_p, []),
+    "tri_model_create": (I, [ctypes.POINTER(ModelDesc), ctypes.POINTER(P), I, ctypes.POINTER(P)]),
+    "tri_model_destroy": (I, [P]),
+    "tri_session_bytes": (I, [P, I, I, I, ctypes.POINTER(SZ)]),
+    "tri_session_create": (I, [P, I, I, I, P, SZ, P, ctypes.POINTER(P)]),
+    "tri_session_destroy": (I, [P]),
+    "tri_prefill": (I, [P, I, IP, I]),
+    "tri_decode_step": (I, [P, I, I, F, IP, ctypes.POINTER(SeqStats)]),
+    "tri_set_lora": (I, [P, I]),
+    "kv_append": (I, [P, I, I]),
+    "kv_rollback": (I, [P, I, I]),
+    "tri_get_state": (I, [P, I, ctypes.POINTER(I), ctypes.POINTER(I), IP, I]),
+    "tri_forward": (I, [P, I, IP, IP, IP, IP, IP, P, IP, FP]),
+    "tri_forward_bytes": (I, [P, I, ctypes.POINTER(ctypes.c_double)]),
+    "tri_set_trace": (I, [P, I]),
+    "tri_trace_count": (I, [P, ctypes.POINTER(I)]),
+    "tri_trace_get": (I, [P, I, ctypes.POINTER(I), IP, IP, IP, IP, IP, FP, I, ctypes.POINTER(I)]),
+    "tri_set_draft_override": (I, [P, I, IP, I, I]),
+    "tri_profile": (I, [P, I]),
+    "tri_profile_read": (I, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]),
+    "block_causal_attn_ws_bytes": (I, [I, I, I, I, I, ctypes.POINTER(SZ)]),
+    "block_causal_attn": (I, [P, P, P, I, P, P, I, I, I, I, I, I, I, F, I, I, P, P, SZ, P]),
+    "sample_commit_ws_bytes": (I, [I, I, ctypes.POINTER(SZ)]),
+    "sample_commit": (I, [P, I, I, P, P, I, F, P, P, P, P, P, SZ, P]),
+    "verify_accept": (I, [P, P, I, I, P, P, P, P]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libtrimode.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m self_speculative_lm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(rc: int) -> None:
+    if rc != TRI_OK:
+        raise TriError(rc, lib().tri_last_error().decode(errors="replace"))

@@ -1,0 +1,400 @@
+// Row-wise kernels of the decode forward and the sampling/acceptance kernels.
+//
+// Every row-wise reduction here runs in a fixed order that depends only on the
+// row's own data and the shape, so a row's result does not depend on which
+// other rows share the launch.
+#include <math.h>
+
+#include "tri_common.h"
+
+namespace tri {
+namespace {
+
+// Sum of the partial slots of column c of row r (slot order).
+__device__ __forceinline__ float slot_sum(const float* P, int nslots, size_t stride, size_t off) {
+  float acc = P[off];
+  for (int s = 1; s < nslots; ++s) acc += P[s * stride + off];
+  return acc;
+}
+
+// Fixed-order block sum over 256 threads.
+__device__ float block_sum_256(float v, float* red) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float t = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return t;
+}
+
+template <typename T>
+__global__ void embed_kernel(const int32_t* tok, const T* E, int d, float* x) {
+  const int r = blockIdx.x;
+  const size_t src = (size_t)tok[r] * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) x[(size_t)r * d + c] = Elem<T>::load(E, src + c);
+}
+
+// x[r] += sum of slots; y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g   (RMSNorm).
+constexpr int NORM_VPT = 32;  // d <= 256 * 32
+template <typename T>
+__global__ __launch_bounds__(256) void resid_norm_kernel(float* x, const float* P, int nslots,
+                                                         size_t stride, int d, const float* g,
+                                                         float eps, T* y) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float* xr = x + (size_t)r * d;
+  float v[NORM_VPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NORM_VPT; ++i) {
+    const int c = tid + i * 256;
+    float val = 0.f;
+    if (c < d) {
+      val = xr[c];
+      if (nslots > 0) {
+        val += slot_sum(P, nslots, stride, (size_t)r * d + c);
+        xr[c] = val;
+      }
+    }
+    v[i] = val;
+    ss += val * val;
+  }
+  const float tot = block_sum_256(ss, red);
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < NORM_VPT; ++i) {
+    const int c = tid + i * 256;
+    if (c < d) Elem<T>::store(y, (size_t)r * d + c, v[i] * inv * g[c]);
+  }
+}
+
+// Sum the QKV slots, rotate q and k (rotate-half pairs (i, i + hd/2) by
+// pos * base^(-2i/hd), cos/sin table precomputed), store q and write k, v
+// into the cache slot of the row's position (V transposed).
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* P, int nslots, size_t stride, int hq,
+                                                      int hkv, int hd, const int32_t* row_seq,
+                                                      const int32_t* row_pos, const float* rope,
+                                                      T* qout, T* kc, T* vc, int ctx, size_t css) {
+  const int r = blockIdx.x;
+  const int pos = row_pos[r], seq = row_seq[r];
+  const int half = hd / 2;
+  const int N = (hq + 2 * hkv) * hd;
+  const size_t rb = (size_t)r * N;
+  const int npair = (hq + hkv) * half;
+  const int total = npair + hkv * hd;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    if (i < npair) {
+      const int h = i / half, c = i - h * half;
+      const int ca = h * hd + c;
+      const float xa = slot_sum(P, nslots, stride, rb + ca);
+      const float xb = slot_sum(P, nslots, stride, rb + ca + half);
+      const float cs = rope[((size_t)pos * half + c) * 2];
+      const float sn = rope[((size_t)pos * half + c) * 2 + 1];
+      const float ra = xa * cs - xb * sn;
+      const float rbv = xb * cs + xa * sn;
+      if (h < hq) {
+        const size_t o = ((size_t)r * hq + h) * hd + c;
+        Elem<T>::store(qout, o, ra);
+        Elem<T>::store(qout, o + half, rbv);
+      } else {
+        const size_t o = (size_t)seq * css + ((size_t)(h - hq) * ctx + pos) * hd + c;
+        Elem<T>::store(kc, o, ra);
+        Elem<T>::store(kc, o + half, rbv);
+      }
+    } else {
+      const int vi = i - npair;
+      const int kh = vi / hd, dd = vi - kh * hd;
+      const float val = slot_sum(P, nslots, stride, rb + (size_t)(hq + hkv) * hd + vi);
+      Elem<T>::store(vc, (size_t)seq * css + ((size_t)kh * hd + dd) * ctx + pos, val);
+    }
+  }
+}
+
+// h = silu(gate) * up with gate = slots of columns [0, ffn), up = [ffn, 2 ffn).
+template <typename T>
+__global__ void swiglu_kernel(const float* P, int nslots, size_t stride, int ffn, T* h) {
+  const int r = blockIdx.x;
+  const size_t rb = (size_t)r * 2 * ffn;
+  for (int c = threadIdx.x; c < ffn; c += blockDim.x) {
+    const float gt = slot_sum(P, nslots, stride, rb + c);
+    const float up = slot_sum(P, nslots, stride, rb + ffn + c);
+    Elem<T>::store(h, (size_t)r * ffn + c, gt / (1.0f + expf(-gt)) * up);
+  }
+}
+
+// LoRA middle activation A o, kept only on flagged rows (zero elsewhere).
+template <typename T>
+__global__ void lora_mid_kernel(const float* P, int nslots, size_t stride, int rk,
+                                const int32_t* row_lora, T* mid) {
+  const int r = blockIdx.x;
+  const bool on = row_lora[r] != 0;
+  for (int c = threadIdx.x; c < rk; c += blockDim.x)
+    Elem<T>::store(mid, (size_t)r * rk + c, on ? slot_sum(P, nslots, stride, (size_t)r * rk + c) : 0.f);
+}
+
+__global__ void zero_kernel(float* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+// ------------------------------------------------------------ vocab reduction
+// Running (max, lowest argmax, sum exp(l - max)) of a stream of logits.
+struct Red {
+  float m;
+  float s;
+  int idx;
+};
+
+__device__ __forceinline__ Red red_merge(Red a, Red b) {
+  if (b.s == 0.f) return a;
+  if (a.s == 0.f) return b;
+  const bool bw = (b.m > a.m) || (b.m == a.m && b.idx < a.idx);
+  const Red w = bw ? b : a, o = bw ? a : b;
+  Red out;
+  out.m = w.m;
+  out.idx = w.idx;
+  out.s = w.s + o.s * expf(o.m - w.m);
+  return out;
+}
+
+constexpr int VCHUNK = 4096;
+
+// Stage 1: grid (chunks, rows); per chunk partial (m, s, idx).
+__global__ __launch_bounds__(256) void vocab_stage1_kernel(const float* logits, int vocab,
+                                                           const int32_t* row_kind, Red* part,
+                                                           int nchunk, int32_t* status) {
+  __shared__ Red sh[256];
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  if (c == 0 && r == 0 && tid == 0) *status = 0;
+  if (row_kind[r] == 0) return;
+  const float* lr = logits + (size_t)r * vocab;
+  Red acc{-INFINITY, 0.f, 0x7fffffff};
+  const int beg = c * VCHUNK, end = min(vocab, beg + VCHUNK);
+  for (int i = beg + tid; i < end; i += 256) {
+    const float x = lr[i];
+    if (x > acc.m) {
+      acc.s = acc.s * expf(acc.m - x) + 1.0f;
+      acc.m = x;
+      acc.idx = i;
+    } else if (x != -INFINITY) {
+      acc.s += expf(x - acc.m);
+    }
+  }
+  sh[tid] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) sh[tid] = red_merge(sh[tid], sh[tid + off]);
+    __syncthreads();
+  }
+  if (tid == 0) part[(size_t)r * nchunk + c] = sh[0];
+}
+
+// Stage 2: one thread per row merges its chunks in order.
+__global__ void vocab_stage2_kernel(const Red* part, int rows, int nchunk, const int32_t* row_kind,
+                                    int32_t* out_tok, float* out_conf, int32_t* out_commit,
+                                    int32_t* status) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const int kind = row_kind[r];
+  if (kind == 0) {
+    out_commit[r] = 0;
+    return;
+  }
+  Red acc = part[(size_t)r * nchunk];
+  for (int c = 1; c < nchunk; ++c) acc = red_merge(acc, part[(size_t)r * nchunk + c]);
+  const float conf = 1.0f / acc.s;
+  const bool finite = isfinite(conf) && isfinite(acc.m) && acc.idx != 0x7fffffff;
+  out_tok[r] = finite ? acc.idx : -1;
+  out_conf[r] = finite ? conf : NAN;
+  out_commit[r] = (kind == 1 && finite) ? 1 : 0;
+  if (!finite) atomicAdd(status, 1);
+}
+
+// Stage 3: one wave per block: threshold commit, at least one.
+__global__ __launch_bounds__(64) void commit_kernel(const int32_t* row_kind, const int32_t* block_start,
+                                                    float threshold, const float* conf,
+                                                    int32_t* out_commit) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int beg = block_start[b], end = block_start[b + 1];
+  bool any = false;
+  float best = -1.f;
+  int bestr = 0x7fffffff;
+  for (int r0 = beg; r0 < end; r0 += 64) {
+    const int r = r0 + lane;
+    bool pass = false;
+    if (r < end && row_kind[r] == 2) {
+      const float c = conf[r];
+      if (isfinite(c)) {
+        pass = c > threshold;
+        if (c > best || (c == best && r < bestr)) {
+          best = c;
+          bestr = r;
+        }
+      }
+      out_commit[r] = pass ? 1 : 0;
+    } else if (r < end && row_kind[r] == 3) {
+      out_commit[r] = 0;
+    }
+    any = any || pass;
+  }
+  any = __any(any);
+  if (any) return;
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ob = __shfl_xor(best, off);
+    const int orr = __shfl_xor(bestr, off);
+    if (ob > best || (ob == best && orr < bestr)) {
+      best = ob;
+      bestr = orr;
+    }
+  }
+  if (lane == 0 && bestr != 0x7fffffff) out_commit[bestr] = 1;
+}
+
+// One wave per sequence: a = first mismatch (or k).
+__global__ __launch_bounds__(64) void verify_accept_kernel(const int32_t* draft, const int32_t* ar,
+                                                           int k, int32_t* accept_len,
+                                                           int32_t* committed, int32_t* kv_len) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  int a = k;
+  for (int i0 = 0; i0 < k; i0 += 64) {
+    const int i = i0 + lane;
+    const bool mis = i < k && draft[(size_t)b * k + i] != ar[(size_t)b * (k + 1) + i];
+    const unsigned long long bal = __ballot(mis);
+    if (bal) {
+      a = i0 + __ffsll((long long)bal) - 1;
+      break;
+    }
+  }
+  for (int i = lane; i <= k; i += 64)
+    committed[(size_t)b * (k + 1) + i] = (i <= a) ? ar[(size_t)b * (k + 1) + i] : -1;
+  if (lane == 0) {
+    accept_len[b] = a;
+    if (kv_len) kv_len[b] += a;
+  }
+}
+
+__global__ void scatter_gather_kernel(const int32_t* src, const int32_t* sidx, const int32_t* didx, int n,
+                                      int32_t* dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[didx[i]] = src[sidx[i]];
+}
+
+}  // namespace
+
+#define TRI_DISPATCH(dtype, F32CALL, BF16CALL) \
+  do {                                         \
+    if ((dtype) == TRI_F32) {                  \
+      F32CALL;                                 \
+    } else {                                   \
+      BF16CALL;                                \
+    }                                          \
+  } while (0)
+
+hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, int d, float* x,
+                        hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  TRI_DISPATCH(dtype,
+               hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, st, tok,
+                                  static_cast<const float*>(E), d, x),
+               hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, tok,
+                                  static_cast<const bf16_t*>(E), d, x));
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, size_t stride, int rows,
+                             int d, const float* g, float eps, void* y, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (d > 256 * NORM_VPT) return hipErrorInvalidValue;
+  TRI_DISPATCH(dtype,
+               hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(rows), dim3(256), 0, st, x, P, nslots,
+                                  stride, d, g, eps, static_cast<float*>(y)),
+               hipLaunchKernelGGL(resid_norm_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, x, P,
+                                  nslots, stride, d, g, eps, static_cast<bf16_t*>(y)));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, int rows, int hq, int hkv,
+                          int hd, const int32_t* row_seq, const int32_t* row_pos, const float* rope,
+                          void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  TRI_DISPATCH(dtype,
+               hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(rows), dim3(256), 0, st, P, nslots, stride,
+                                  hq, hkv, hd, row_seq, row_pos, rope, static_cast<float*>(qout),
+                                  static_cast<float*>(kc), static_cast<float*>(vc), ctx, css),
+               hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, P, nslots,
+                                  stride, hq, hkv, hd, row_seq, row_pos, rope,
+                                  static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
+                                  static_cast<bf16_t*>(vc), ctx, css));
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t stride, int rows, int ffn, void* h,
+                         hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  TRI_DISPATCH(dtype,
+               hipLaunchKernelGGL(swiglu_kernel<float>, dim3(rows), dim3(256), 0, st, P, nslots, stride,
+                                  ffn, static_cast<float*>(h)),
+               hipLaunchKernelGGL(swiglu_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, P, nslots, stride,
+                                  ffn, static_cast<bf16_t*>(h)));
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_mid(int dtype, const float* P, int nslots, size_t stride, int rows, int rk,
+                           const int32_t* row_lora, void* mid, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  TRI_DISPATCH(dtype,
+               hipLaunchKernelGGL(lora_mid_kernel<float>, dim3(rows), dim3(128), 0, st, P, nslots, stride,
+                                  rk, row_lora, static_cast<float*>(mid)),
+               hipLaunchKernelGGL(lora_mid_kernel<bf16_t>, dim3(rows), dim3(128), 0, st, P, nslots,
+                                  stride, rk, row_lora, static_cast<bf16_t*>(mid)));
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks > 4096 ? 4096 : (unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+size_t vocab_ws_bytes(int rows, int vocab) {
+  const int nchunk = (vocab + VCHUNK - 1) / VCHUNK;
+  return (size_t)rows * nchunk * sizeof(Red) + 256;
+}
+
+hipError_t launch_sample_commit(const float* logits, int rows, int vocab, const int32_t* row_kind,
+                                const int32_t* block_start, int n_blocks, float threshold,
+                                int32_t* out_tok, float* out_conf, int32_t* out_commit,
+                                int32_t* out_status, void* ws, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int nchunk = (vocab + VCHUNK - 1) / VCHUNK;
+  Red* part = static_cast<Red*>(ws);
+  hipLaunchKernelGGL(vocab_stage1_kernel, dim3(nchunk, rows), dim3(256), 0, st, logits, vocab, row_kind,
+                     part, nchunk, out_status);
+  hipLaunchKernelGGL(vocab_stage2_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, part, rows, nchunk,
+                     row_kind, out_tok, out_conf, out_commit, out_status);
+  if (n_blocks > 0)
+    hipLaunchKernelGGL(commit_kernel, dim3(n_blocks), dim3(64), 0, st, row_kind, block_start, threshold,
+                       out_conf, out_commit);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_accept(const int32_t* draft, const int32_t* ar_tok, int batch, int k,
+                                int32_t* accept_len, int32_t* committed, int32_t* kv_len,
+                                hipStream_t st) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(verify_accept_kernel, dim3(batch), dim3(64), 0, st, draft, ar_tok, k, accept_len,
+                     committed, kv_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_gather(const int32_t* src, const int32_t* sidx, const int32_t* didx, int n,
+                                 int32_t* dst, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_gather_kernel, dim3((n + 255) / 256), dim3(256), 0, st, src, sidx, didx, n, dst);
+  return hipGetLastError();
+}
+
+}  // namespace tri

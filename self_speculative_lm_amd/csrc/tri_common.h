@@ -1,0 +1,100 @@
+// Internal declarations shared by the gfx950 kernels and the runtime of
+// libtrimode.so.  Not part of the public C-ABI (see include/trimode.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "trimode.h"
+
+namespace tri {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // raw bfloat16 storage
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float32 -> bfloat16 (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Element access for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ static void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ static float load(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ static void store(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  All are asynchronous.
+
+// Y partial slots: P[s][m][n] (float32), s < S, for Y = X W^T where the rows of
+// W are the concatenation of up to three segments (each [rows][K]).
+struct WSeg {
+  const void* ptr;
+  int rows;
+};
+struct GemmPlan {
+  int S;   // K splits
+  int Ks;  // K per split (multiple of 32)
+};
+GemmPlan gemm_plan(int N, int K, int dtype);
+hipError_t launch_gemm(int dtype, const void* X, int M, int K, const WSeg* segs, int nseg, int N,
+                       const GemmPlan& plan, float* P, size_t slot_stride, hipStream_t st);
+
+struct AttnLaunch {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* seq_start;
+  const int32_t* slot_seq;  // cache sequence of each slot (NULL = identity)
+  const int32_t* row_hi;
+  int n_seq, rows, max_rows_per_seq, max_hi;
+  int hq, hkv, hd, ctx;
+  float scale;
+  int kv_split;
+  void* out;
+  float* part;  // split partials
+};
+int attn_pick_split(int max_hi);
+size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split);
+hipError_t launch_attn(int dtype, const AttnLaunch& a, hipStream_t st);
+
+// Misc kernels.
+hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, int d, float* x,
+                        hipStream_t st);
+hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, size_t slot_stride,
+                             int rows, int d, const float* g, float eps, void* y, hipStream_t st);
+hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
+                          int hq, int hkv, int hd, const int32_t* row_seq, const int32_t* row_pos,
+                          const float* rope, void* qout, void* kc, void* vc, int ctx,
+                          size_t cache_seq_stride, hipStream_t st);
+hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
+                         int ffn, void* h, hipStream_t st);
+hipError_t launch_lora_mid(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
+                           int r, const int32_t* row_lora, void* mid, hipStream_t st);
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);
+size_t vocab_ws_bytes(int rows, int vocab);
+hipError_t launch_scatter_gather(const int32_t* src, const int32_t* sidx, const int32_t* didx, int n,
+                                 int32_t* dst, hipStream_t st);
+hipError_t launch_sample_commit(const float* logits, int rows, int vocab, const int32_t* row_kind,
+                                const int32_t* block_start, int n_blocks, float threshold,
+                                int32_t* out_tok, float* out_conf, int32_t* out_commit,
+                                int32_t* out_status, void* ws, hipStream_t st);
+hipError_t launch_verify_accept(const int32_t* draft, const int32_t* ar_tok, int batch, int k,
+                                int32_t* accept_len, int32_t* committed, int32_t* kv_len,
+                                hipStream_t st);
+
+}  // namespace tri

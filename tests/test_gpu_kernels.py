@@ -1,0 +1,202 @@
+"""GPU parity of the kernel-level C-ABI entry points against the oracle:
+block_causal_attn, sample_commit and verify_accept."""
+import math
+
+import numpy as np
+import pytest
+
+import seeded
+from oracle.model import attend
+from oracle.sampler import accept_length, commit_set, vocab_reduce
+
+pytestmark = pytest.mark.gpu
+
+# bf16 attention bound: the output is rounded to bf16 (<= 2^-9 relative of
+# max|v|) and the probabilities enter P.V as bf16 (another <= 2^-9 of max|v|);
+# with N(0,1) values max|v| < 6, so |err| <= 2 * 2^-9 * 6 ~ 2.3e-2.
+ATT_TOL_BF16 = 2.5e-2
+ATT_TOL_F32 = 2e-5
+
+
+def _attn_case(prefixes, nrows, hq, hkv, hd, bf16, causal=False, kv_split=0, seed=3, sample=None):
+    import torch
+    import self_speculative_lm_amd as tm
+    b = len(prefixes)
+    maxlen = max(p + n for p, n in zip(prefixes, nrows))
+    ctx = (maxlen + 63) // 64 * 64
+    R = max(nrows)
+    q, k, v = seeded.attention_operands(R, max(prefixes), hq, hkv, hd, batch=b, bf16=bf16, seed=seed)
+    # k, v: [b, Pmax + R, hkv, hd]; sequence s uses positions [0, P_s + n_s)
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    kc = torch.zeros((b, hkv, ctx, hd), dtype=tdt)
+    vc = torch.zeros((b, hkv, hd, ctx), dtype=tdt)
+    qs, his, starts = [], [], [0]
+    for s in range(b):
+        L = prefixes[s] + nrows[s]
+        kc[s, :, :L] = torch.from_numpy(k[s, :L]).permute(1, 0, 2).to(tdt)
+        vc[s, :, :, :L] = torch.from_numpy(v[s, :L]).permute(1, 2, 0).to(tdt)
+        qs.append(q[s, : nrows[s]])
+        for i in range(nrows[s]):
+            his.append(prefixes[s] + i + 1 if causal else L)
+        starts.append(starts[-1] + nrows[s])
+    qn = np.concatenate(qs)
+    dev = "cuda"
+    tq = torch.from_numpy(qn).to(tdt).to(dev)
+    out = torch.zeros_like(tq)
+    seq_start = torch.tensor(starts, dtype=torch.int32, device=dev)
+    row_hi = torch.tensor(his, dtype=torch.int32, device=dev)
+    tm.block_causal_attn(tq, kc.to(dev), vc.to(dev), seq_start, row_hi, out, 1.0 / math.sqrt(hd),
+                         max_rows_per_seq=R, max_hi=max(his), kv_split=kv_split)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    rows = list(range(len(his))) if sample is None else sample
+    err = 0.0
+    for r in rows:
+        s = int(np.searchsorted(starts, r, side="right") - 1)
+        K = k[s].astype(np.float64)
+        V = v[s].astype(np.float64)
+        ref = attend(qn[r].astype(np.float64), K, V, his[r], hq // hkv)
+        err = max(err, float(np.abs(ref - got[r]).max()))
+    return err
+
+
+@pytest.mark.parametrize("prefixes,nrows,causal,kv_split", [
+    ([0], [33], False, 64),
+    ([37], [33], False, 64),
+    ([31], [33], False, 0),
+    ([700], [32], True, 256),
+    ([200], [1], False, 0),
+    ([5, 130, 300], [1, 33, 8], False, 128),
+    ([64, 1], [64, 63], True, 64),
+])
+def test_block_causal_attn_bf16_matches_oracle(prefixes, nrows, causal, kv_split):
+    err = _attn_case(prefixes, nrows, 32, 8, 128, True, causal, kv_split)
+    assert err <= ATT_TOL_BF16, err
+
+
+def test_block_causal_attn_bf16_group5():
+    assert _attn_case([100], [33], 40, 8, 128, True, False, 64) <= ATT_TOL_BF16
+
+
+@pytest.mark.parametrize("prefixes,nrows,hq,hkv,hd,causal", [
+    ([0], [8], 4, 4, 32, False), ([50], [9], 4, 4, 32, True), ([20, 70], [9, 16], 4, 2, 64, False),
+    ([100], [3], 2, 1, 128, False),
+])
+def test_block_causal_attn_f32_matches_oracle(prefixes, nrows, hq, hkv, hd, causal):
+    err = _attn_case(prefixes, nrows, hq, hkv, hd, False, causal)
+    assert err <= ATT_TOL_F32, err
+
+
+@pytest.mark.parametrize("prefix,batch,causal", [(512, 1, False), (2048, 8, False), (8192, 1, True),
+                                                 (32768, 1, False), (32768, 8, False)])
+def test_block_causal_attn_full_size_sampled(prefix, batch, causal):
+    """Attention-alone shapes (32 q / 8 kv heads, hd 128, 32-row block) at the
+    benchmark's launch configuration, checked on sampled rows."""
+    rng = np.random.default_rng(prefix + batch)
+    sample = sorted(set(rng.integers(0, 32 * batch, 6).tolist() + [0, 32 * batch - 1]))
+    err = _attn_case([prefix] * batch, [32] * batch, 32, 8, 128, True, causal, 0, sample=sample)
+    assert err <= ATT_TOL_BF16, err
+
+
+def test_block_causal_attn_rejects_bad_arguments():
+    import torch
+    import self_speculative_lm_amd as tm
+    q = torch.zeros((4, 8, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((1, 2, 100, 128), dtype=torch.bfloat16, device="cuda")  # ctx not a multiple of 64
+    vc = torch.zeros((1, 2, 128, 100), dtype=torch.bfloat16, device="cuda")
+    ss = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    hi = torch.full((4,), 10, dtype=torch.int32, device="cuda")
+    with pytest.raises(tm.TriError):
+        tm.block_causal_attn(q, kc, vc, ss, hi, torch.zeros_like(q), 0.1, max_rows_per_seq=4, max_hi=10)
+
+
+# ----------------------------------------------------------------- sampler
+def _sampler_case(rows, vocab, seed, kinds, blocks, tau, plant=None):
+    import torch
+    import self_speculative_lm_amd as tm
+    lg = seeded.logits_matrix(rows, vocab, seed, 1.0)
+    if plant:
+        plant(lg)
+    dev = "cuda"
+    tl = torch.from_numpy(lg).to(dev)
+    kind = torch.tensor(kinds, dtype=torch.int32, device=dev)
+    bs = torch.tensor(blocks, dtype=torch.int32, device=dev) if blocks else None
+    ot = torch.zeros(rows, dtype=torch.int32, device=dev)
+    oc = torch.zeros(rows, dtype=torch.float32, device=dev)
+    om = torch.zeros(rows, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    tm.sample_commit(tl, kind, bs, tau, ot, oc, om, st)
+    torch.cuda.synchronize()
+    return lg, ot.cpu().numpy(), oc.cpu().numpy(), om.cpu().numpy(), int(st.item())
+
+
+@pytest.mark.parametrize("vocab", [1000, 151936])
+@pytest.mark.parametrize("tau", [0.0, 0.5, 0.9, 1.0])
+def test_sample_commit_matches_oracle(vocab, tau):
+    rows = 33
+    kinds = [1] + [2] * 20 + [3, 2, 2, 3, 2, 2, 3, 2, 2, 2, 2, 2]
+    blocks = [1, 17, 33]
+
+    def plant(lg):
+        lg[3, 7] = lg[3].max() + 30.0     # very confident: passes any tau < 1
+        lg[20, 11] = lg[20].max() + 2.0
+        lg[25, 100] = lg[25, 200] = lg[25].max() + 25.0   # exact tie: lowest id, conf ~ 0.5
+        lg[30, :] = 0.0                                   # all equal: id 0, conf 1/V
+
+    lg, tok, conf, com, st = _sampler_case(rows, vocab, 17 + vocab, kinds, blocks, tau, plant)
+    assert st == 0
+    ref = [vocab_reduce(lg[r].astype(np.float64)) if kinds[r] else (0, 0.0) for r in range(rows)]
+    for r in range(rows):
+        if kinds[r] == 0:
+            continue
+        assert tok[r] == ref[r][0], r
+        assert conf[r] == pytest.approx(ref[r][1], rel=2e-6), r
+    assert com[0] == 1
+    for b in range(len(blocks) - 1):
+        lo, hi = blocks[b], blocks[b + 1]
+        el = [kinds[r] == 2 for r in range(lo, hi)]
+        cf = [ref[r][1] for r in range(lo, hi)]
+        flagged = any(abs(c - tau) < 1e-6 for c, e in zip(cf, el) if e)
+        want = set(lo + i for i in commit_set(cf, el, tau))
+        gotc = set(r for r in range(lo, hi) if com[r])
+        if not flagged:
+            assert gotc == want, (b, gotc, want)
+
+
+def test_sample_commit_flags_non_finite_rows():
+    kinds = [1, 1, 2, 2]
+
+    def plant(lg):
+        lg[1, 5] = np.nan
+
+    _, tok, conf, com, st = _sampler_case(4, 512, 5, kinds, [2, 4], 0.5, plant)
+    assert st == 1 and com[1] == 0 and tok[1] == -1
+    assert com[0] == 1
+
+
+# ------------------------------------------------------------------ verify
+@pytest.mark.parametrize("k", [1, 8, 32, 64])
+def test_verify_accept_matches_oracle(k):
+    import torch
+    import self_speculative_lm_amd as tm
+    b = 16
+    d, g = seeded.token_pairs(b, k, 50, seed=k, match_prob=0.85)
+    d[0] = g[0, :k]          # all match -> a = k
+    d[1, 0] = (g[1, 0] + 1) % 50   # immediate mismatch -> a = 0
+    dev = "cuda"
+    td = torch.from_numpy(d).to(dev)
+    tg = torch.from_numpy(g).to(dev)
+    acc = torch.zeros(b, dtype=torch.int32, device=dev)
+    com = torch.zeros((b, k + 1), dtype=torch.int32, device=dev)
+    kvl = torch.arange(b, dtype=torch.int32, device=dev) * 10
+    tm.verify_accept(td, tg, acc, com, kvl)
+    torch.cuda.synchronize()
+    acc, com, kvl = acc.cpu().numpy(), com.cpu().numpy(), kvl.cpu().numpy()
+    for i in range(b):
+        a = accept_length(list(d[i]), list(g[i]))
+        assert acc[i] == a
+        assert list(com[i, : a + 1]) == list(g[i, : a + 1])
+        assert (com[i, a + 1:] == -1).all()
+        assert kvl[i] == 10 * i + a
+        assert 1 <= a + 1 <= k + 1
+    assert acc[0] == k and acc[1] == 0

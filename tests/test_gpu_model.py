@@ -1,0 +1,182 @@
+"""End-to-end GPU parity of tri_decode_step in the three modes against the
+oracle: free-running token sequences, teacher-forced logits (every traced
+forward replayed through the oracle), batch invariance (GPU self-speculation
+equals GPU AR), LoRA on the drafter only, ragged batches and state errors."""
+import numpy as np
+import pytest
+
+import seeded
+from oracle import MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC, OracleModel, OracleSession
+from oracle.sampler import vocab_reduce
+from tests.gpu_util import device_weights, make_model, replay, top2_margin
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+_models = {}
+
+
+def get(shape):
+    if shape.name not in _models:
+        arrays = seeded.gen_weights(shape)
+        tens = device_weights(shape, arrays)
+        _models[shape.name] = (arrays, tens, make_model(shape, tens), OracleModel(shape, arrays))
+    return _models[shape.name]
+
+
+def gpu_generate(shape, mode, n_new, block, tau=0.9, prompt_len=16, max_ctx=128, lora=False, trace=False,
+                 prompts=None):
+    import self_speculative_lm_amd as tm
+    arrays, tens, model, om = get(shape)
+    prompts = prompts or [seeded.prompt(prompt_len, shape.vocab)]
+    sess = tm.Session(model, max_batch=len(prompts), max_ctx=max_ctx, max_rows=64 * len(prompts))
+    if lora:
+        sess.set_lora(True)
+    if trace:
+        sess.set_trace(True)
+    for i, p in enumerate(prompts):
+        sess.prefill(i, p)
+    outs = [[] for _ in prompts]
+    stats = []
+    gmode = {MODE_AR: tm.TRI_AR, MODE_DIFFUSION: tm.TRI_DIFFUSION, MODE_SELFSPEC: tm.TRI_SELFSPEC}[mode]
+    while min(len(o) for o in outs) < n_new:
+        toks, st = sess.decode_step(gmode, block, tau)
+        stats.append(st)
+        for i in range(len(prompts)):
+            outs[i] += [int(t) for t in toks[i] if t >= 0]
+    return [o[:n_new] for o in outs], stats, sess
+
+
+def oracle_generate(shape, mode, n_new, block, tau=0.9, prompt_len=16, max_ctx=128, lora=False, prompt=None):
+    _, _, _, om = get(shape)
+    o = OracleSession(om, max_ctx)
+    o.prefill(prompt if prompt is not None else seeded.prompt(prompt_len, shape.vocab))
+    return o.generate(mode, n_new, block=block, threshold=tau, lora=lora), o
+
+
+def teacher_forced_error(shape, sess, max_ctx=128):
+    _, _, _, om = get(shape)
+    tr = sess.trace()
+    ref = replay(shape, om, tr, max_ctx)
+    err = 0.0
+    for r, t in zip(ref, tr):
+        if r is not None:
+            err = max(err, float(np.abs(r - t["logits"]).max()))
+    return err, tr, ref
+
+
+@pytest.mark.parametrize("shape", [seeded.TINY, seeded.TINY_SHARP])
+@pytest.mark.parametrize("mode", [MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC])
+def test_tiny_f32_free_running_matches_oracle(shape, mode):
+    got, _, sess = gpu_generate(shape, mode, 32, 8, trace=True)
+    want, _ = oracle_generate(shape, mode, 32, 8)
+    err, _, _ = teacher_forced_error(shape, sess)
+    assert err <= TOL_F32, err
+    assert got[0] == want
+
+
+def test_tiny_selfspec_equals_ar_and_accept_range():
+    shape = seeded.TINY_SHARP
+    ar, _, _ = gpu_generate(shape, MODE_AR, 40, 1)
+    ss, stats, _ = gpu_generate(shape, MODE_SELFSPEC, 40, 8)
+    assert ss == ar
+    for st in stats:
+        n, f, a, _ = st[0]
+        assert 0 <= a <= 8 and n == a + 1 and f == 2
+
+
+def test_tiny_lora_drafter_is_lossless():
+    shape = seeded.TINY_LORA
+    ar, _, _ = gpu_generate(shape, MODE_AR, 32, 1)
+    ss, _, sess = gpu_generate(shape, MODE_SELFSPEC, 32, 8, lora=True, trace=True)
+    assert ss == ar
+    err, tr, _ = teacher_forced_error(shape, sess)
+    assert err <= TOL_F32, err
+    assert any(t["lora"].any() for t in tr)
+    want, _ = oracle_generate(shape, MODE_SELFSPEC, 32, 8, lora=True)
+    assert ss[0] == want
+
+
+def test_tiny_ragged_batch_diffusion_and_selfspec():
+    shape = seeded.TINY_SHARP
+    prompts = [seeded.prompt(16, shape.vocab, stream=i) for i in range(3)]
+    prompts[1] = prompts[1][:9]
+    for mode in (MODE_DIFFUSION, MODE_SELFSPEC, MODE_AR):
+        got, _, _ = gpu_generate(shape, mode, 24, 8, prompts=prompts)
+        for i, p in enumerate(prompts):
+            want, _ = oracle_generate(shape, mode, 24, 8, prompt=p)
+            assert got[i] == want, (mode, i)
+
+
+@pytest.mark.parametrize("shape", [seeded.SMALL_BF16, seeded.SMALL_BF16_SHARP])
+def test_small_bf16_teacher_forced_and_batch_invariant(shape):
+    ar, _, sess_ar = gpu_generate(shape, MODE_AR, 24, 1, prompt_len=40, trace=True)
+    ss, _, sess_ss = gpu_generate(shape, MODE_SELFSPEC, 24, 32, prompt_len=40, trace=True)
+    assert ss == ar                                      # GPU batch invariance: bit-identical decisions
+    tol = TOL_BF16 * shape.lm_head_scale                 # logits scale with the lm_head
+    for sess in (sess_ar, sess_ss):
+        err, tr, ref = teacher_forced_error(shape, sess)
+        assert err <= tol, err
+        # a greedy decision of the GPU differs from the oracle's only where the
+        # oracle's top-2 margin is within twice the logit error (a near-tie)
+        decisions = flips = 0
+        for r, t in zip(ref, tr):
+            if r is None:
+                continue
+            for i in range(len(r)):
+                decisions += 1
+                if int(np.argmax(t["logits"][i])) != vocab_reduce(r[i])[0]:
+                    assert top2_margin(r[i]) <= 2 * err
+                    flips += 1
+        assert flips <= 0.1 * decisions
+
+
+def test_small_bf16_diffusion_teacher_forced():
+    shape = seeded.SMALL_BF16_SHARP
+    got, stats, sess = gpu_generate(shape, MODE_DIFFUSION, 64, 32, tau=0.7, prompt_len=64, trace=True)
+    err, _, _ = teacher_forced_error(shape, sess)
+    assert err <= TOL_BF16 * shape.lm_head_scale, err
+    assert all(t < shape.vocab for t in got[0])
+
+
+def test_small_bf16_lora_lossless():
+    shape = seeded.SMALL_BF16_LORA
+    ar, _, _ = gpu_generate(shape, MODE_AR, 16, 1, prompt_len=32)
+    ss, _, sess = gpu_generate(shape, MODE_SELFSPEC, 16, 32, prompt_len=32, lora=True, trace=True)
+    assert ss == ar
+    err, _, _ = teacher_forced_error(shape, sess)
+    assert err <= TOL_BF16, err
+
+
+def test_state_errors_and_kv_bookkeeping():
+    import self_speculative_lm_amd as tm
+    shape = seeded.TINY
+    _, _, model, _ = get(shape)
+    sess = tm.Session(model, max_batch=2, max_ctx=40, max_rows=16)
+    with pytest.raises(tm.TriError) as e:
+        sess.decode_step(tm.TRI_AR, 1)
+    assert e.value.code == tm._lib.TRI_ESTATE
+    sess.prefill(0, seeded.prompt(30, shape.vocab))
+    toks, kv = sess.state(0)
+    assert len(toks) == 30 and kv == 29
+    with pytest.raises(tm.TriError):
+        sess.kv_append(0, 1)                      # nothing written beyond the prefix
+    sess.kv_rollback(0, 4)
+    assert sess.state(0)[1] == 25
+    with pytest.raises(tm.TriError):
+        sess.kv_rollback(0, 26)
+    with pytest.raises(tm.TriError):
+        sess.decode_step(tm.TRI_SELFSPEC, 32)      # 30 + 33 > max_ctx
+    with pytest.raises(tm.TriError):
+        sess.decode_step(tm.TRI_DIFFUSION, 8, 1.5)  # bad threshold
+    # a rollback makes tokens pending again: the next AR step re-runs them
+    out, st = sess.decode_step(tm.TRI_AR, 1)
+    assert st[0][0] == 1
+    toks2, kv2 = sess.state(0)
+    assert len(toks2) == 31 and kv2 == 30
+    # same result as a fresh session that never rolled back
+    s2 = tm.Session(model, max_batch=1, max_ctx=40, max_rows=16)
+    s2.prefill(0, seeded.prompt(30, shape.vocab))
+    out2, _ = s2.decode_step(tm.TRI_AR, 1)
+    assert out2[0, 0] == out[0, 0]

@@ -1,0 +1,230 @@
+"""Benchmark of the tri-mode decode step on one MI355X.
+
+Default workload: the 8B-class decoder (36 layers, d 4096, 32 q / 8 kv heads
+x 128, SwiGLU 12288, vocab 151936 + [MASK]), bf16 random-init N(0, 0.02),
+self-speculation at batch 1 with draft block 32, temperature 0, after a
+512-token uniform-random prompt.  One step = one self-speculation round (a
+draft forward over 33 rows and a verify forward over 32 rows, sampling and
+acceptance), i.e. one pass of the whole decode path.
+
+Prints one JSON line: committed tokens/s over the timed rounds, TPF/TPR, the
+roofline of the dominant kernel (the gate/up projection GEMM) timed with HIP
+events on the session stream, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-replay]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "committed tokens/s @bs1, 8B-class self-spec block 32; TPF; % HBM roofline"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def upload_weights(shape, device):
+    import torch
+    import seeded
+    tensors = {}
+    for i, (name, shp, kind) in enumerate(seeded.weight_specs(shape)):
+        _, a = seeded.gen_weight(shape, i)
+        t = torch.from_numpy(a)
+        t = t.to(torch.float32) if kind == "ones" else t.to(torch.bfloat16)
+        tensors[name] = t.to(device, non_blocking=False)
+        del a, t
+    return tensors
+
+
+def gu_bytes_per_launch(shape, rows):
+    """Algorithmic bytes of one gate/up GEMM launch: both weight matrices once,
+    the normed activations once, the float32 outputs once."""
+    d, f = shape.d_model, shape.d_ffn
+    return 2 * f * d * 2 + rows * d * 2 + rows * 2 * f * 4
+
+
+def cpu_baseline(shape, prefix, k, tpr):
+    """The oracle on the host cores: one draft forward (1 + k rows) and one
+    verify forward (k rows) over 1- and 2-layer slices of the model with a
+    prefix-long cache, extrapolated to all layers (per-layer time = t2 - t1)."""
+    import dataclasses
+
+    import numpy as np
+    import seeded
+    from oracle.model import KVCache, OracleModel, Row, forward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    times = {}
+    for nl in (1, 2):
+        sl = dataclasses.replace(shape, name=f"{shape.name}-slice{nl}", n_layers=nl)
+        om = OracleModel(sl, seeded.gen_weights(sl), batched_linear=True, keep_float32=True)
+        cache = KVCache(sl, prefix + k + 1)
+        rng = np.random.default_rng(0)
+        for arr in (cache.k, cache.v):
+            arr[:, :prefix] = rng.standard_normal(arr[:, :prefix].shape).astype(np.float32)
+        L = prefix + 1
+        draft = [Row(1, L - 1, L)] + [Row(shape.vocab, L + i, L + k, False) for i in range(k)]
+        verify = [Row(2 + i, L + i, L + i + 1) for i in range(k)]
+        t0 = time.perf_counter()
+        forward(om, cache, draft)
+        forward(om, cache, verify)
+        times[nl] = time.perf_counter() - t0
+        del om, cache
+    per_layer = times[2] - times[1]
+    head = times[1] - per_layer
+    round_s = head + shape.n_layers * per_layer
+    return {"value": round(tpr / round_s, 4), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 oracle, one draft ({k + 1} rows) + one verify ({k} rows) forward over 1- and "
+                       f"2-layer slices of the 8B-class model with a {prefix}-token cache; per-layer time "
+                       f"{per_layer:.2f}s, lm_head+sampling {head:.2f}s, extrapolated to {shape.n_layers} layers "
+                       f"= {round_s:.1f}s per round at the GPU's measured {tpr:.2f} tokens/round"),
+            "seconds_measured": round(times[1] + times[2], 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--prompt", type=int, default=512)
+    ap.add_argument("--block", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-replay", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the decode step is built and measured on a single "
+              "MI355X (no multi-GPU path in this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import seeded
+    import self_speculative_lm_amd as tm
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    shape = seeded.MODEL_8B
+    k = args.block
+    t0 = time.time()
+    log(f"generating and uploading {shape.n_params() / 1e9:.2f}B seeded weights")
+    tensors = upload_weights(shape, dev)
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f}s")
+    model = tm.Model(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn,
+                     shape.vocab, tensors, dtype=tm.TRI_BF16)
+    max_ctx = args.prompt + (k + 1) * (args.steps + args.warmup + 2) + 64
+    sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=128, device=dev)
+    prompt = seeded.prompt(args.prompt, shape.vocab)
+    t1 = time.perf_counter()
+    sess.prefill(0, prompt)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t1
+    log(f"prefill of {args.prompt} tokens: {prefill_s * 1e3:.1f} ms")
+
+    for _ in range(args.warmup):
+        sess.decode_step(tm.TRI_SELFSPEC, k)
+    torch.cuda.synchronize()
+    L0 = len(sess.state(0)[0])
+    sess.profile(0)  # gate/up GEMM launches
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    committed, accepts = 0, []
+    for _ in range(args.steps):
+        _, st = sess.decode_step(tm.TRI_SELFSPEC, k)
+        committed += st[0][0]
+        accepts.append(st[0][2])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    gu_ms, gu_n = sess.profile_read()
+    sess.profile(-1)
+    L1 = len(sess.state(0)[0])
+    assert L1 - L0 == committed
+    ms_per_step = elapsed * 1e3 / args.steps
+    forwards = 2 * args.steps
+    tpf = committed / forwards
+    tpr = committed / args.steps
+    value = committed / elapsed
+    log(f"{args.steps} rounds in {elapsed:.3f}s: {value:.1f} tok/s, TPR {tpr:.2f}, {ms_per_step:.2f} ms/round")
+
+    # whole-forward HBM fraction: algorithmic bytes of the two forwards of a round
+    rows_draft = k + 1
+    fwd_bytes = sess.forward_bytes(rows_draft) + sess.forward_bytes(k)
+    round_gbs = fwd_bytes / (elapsed / args.steps) / 1e9
+    gu_avg_ms = gu_ms / max(gu_n, 1)
+    gu_rows = (rows_draft + k) / 2
+    gu_bytes = gu_bytes_per_launch(shape, gu_rows)
+    gu_gbs = gu_bytes / (gu_avg_ms * 1e-3) / 1e9
+    log(f"gate/up GEMM: {gu_n} launches, avg {gu_avg_ms * 1e3:.1f} us -> {gu_gbs:.0f} GB/s")
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights, uniform random prompt)",
+        "config": {"workload": "8B-class tri-mode decoder, self-speculation, batch 1, draft block 32, T=0, "
+                               f"{args.prompt}-token prompt", "layers": shape.n_layers, "d_model": shape.d_model,
+                   "heads": f"{shape.n_q_heads}q/{shape.n_kv_heads}kv x {shape.head_dim}", "d_ffn": shape.d_ffn,
+                   "vocab": shape.vocab, "batch": 1, "block": k, "prompt": args.prompt},
+        "tpf": round(tpf, 4), "tokens_per_round": round(tpr, 4),
+        "accept_hist": {str(a): accepts.count(a) for a in sorted(set(accepts))},
+        "forward_ms": round(elapsed * 1e3 / forwards, 4),
+        "round_hbm_fraction": round(round_gbs / HBM_PEAK_GBS, 4),
+        "round_algorithmic_GBps": round(round_gbs, 1),
+        "prefill_ms": round(prefill_s * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemm_bf16_kernel (gate/up projection, N=24576, K=4096)",
+                     "avg_launch_us": round(gu_avg_ms * 1e3, 2), "launches": gu_n,
+                     "algorithmic_bytes_per_launch": int(gu_bytes)},
+    }
+
+    if not args.no_replay:
+        # controlled-acceptance replay: drafts replaced by the GPU's own greedy AR
+        # continuation up to a*, mismatch forced at a*; every kernel still runs.
+        n_ref = 17 * (k + 1) + k + 2
+        sess.prefill(0, prompt)
+        for _ in range(n_ref):
+            sess.decode_step(tm.TRI_AR, 1)
+        ref = sess.state(0)[0]
+        rep = {}
+        for a_star in (6, k):
+            sess.prefill(0, prompt)
+            sess.set_draft_override(0, ref, a_star)
+            sess.decode_step(tm.TRI_SELFSPEC, k)
+            torch.cuda.synchronize()
+            ts = time.perf_counter()
+            c = 0
+            for _ in range(16):
+                _, st = sess.decode_step(tm.TRI_SELFSPEC, k)
+                c += st[0][0]
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - ts
+            got = sess.state(0)[0]
+            ok = got == ref[: len(got)]
+            rep[str(a_star)] = {"tok_s": round(c / dt, 1), "tokens_per_round": c / 16, "tpf": c / 32,
+                                "matches_ar": bool(ok)}
+            sess.set_draft_override(0, None, -1)
+        result["controlled_acceptance"] = rep
+        log(f"controlled acceptance: {rep}")
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        del sess, model, tensors
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(shape, args.prompt, k, tpr)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

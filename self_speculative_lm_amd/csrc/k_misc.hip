@@ -28,11 +28,15 @@ __device__ float block_sum_256(float v, float* red) {
   return t;
 }
 
+// x[r] = E[tok[r]]; an id outside [0, n_emb) (e.g. the -1 the sampler writes
+// for a row with non-finite logits) gives a zero row instead of a stray read.
 template <typename T>
-__global__ void embed_kernel(const int32_t* tok, const T* E, int d, float* x) {
+__global__ void embed_kernel(const int32_t* tok, const T* E, int n_emb, int d, float* x) {
   const int r = blockIdx.x;
-  const size_t src = (size_t)tok[r] * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) x[(size_t)r * d + c] = Elem<T>::load(E, src + c);
+  const int t = tok[r];
+  const bool ok = t >= 0 && t < n_emb;
+  const size_t src = (size_t)(ok ? t : 0) * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) x[(size_t)r * d + c] = ok ? Elem<T>::load(E, src + c) : 0.f;
 }
 
 // x[r] += sum of slots; y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g   (RMSNorm).
@@ -292,14 +296,14 @@ __global__ void scatter_gather_kernel(const int32_t* src, const int32_t* sidx, c
     }                                          \
   } while (0)
 
-hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, int d, float* x,
+hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, int n_emb, int d, float* x,
                         hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   TRI_DISPATCH(dtype,
                hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, st, tok,
-                                  static_cast<const float*>(E), d, x),
+                                  static_cast<const float*>(E), n_emb, d, x),
                hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, tok,
-                                  static_cast<const bf16_t*>(E), d, x));
+                                  static_cast<const bf16_t*>(E), n_emb, d, x));
   return hipGetLastError();
 }
 

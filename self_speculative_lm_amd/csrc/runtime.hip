@@ -169,6 +169,8 @@ struct tri_session {
   bool lora_on = false;
   bool tracing = false;
   std::vector<TraceRec> trace;
+  hipEvent_t meta_ev[2] = {nullptr, nullptr};  // recorded after each metadata upload
+  bool meta_pending[2] = {false, false};
   int prof_class = -1;
   std::vector<hipEvent_t> ev;  // start/stop pairs
   size_t ev_used = 0;
@@ -272,8 +274,16 @@ int prof_end(tri_session* s, int cls, size_t slot) {
   } while (0)
 
 // ------------------------------------------------------------------ forward
-void stage_meta(tri_session* s, int which, const HostRows& R, const std::vector<int32_t>& sidx,
-                const std::vector<int32_t>& didx) {
+// The pinned host mirror of a metadata set is the source of an asynchronous
+// copy: before it is rewritten, wait until the GPU has consumed the previous
+// upload of that set (back-to-back forwards, e.g. prefill chunks, would
+// otherwise upload another forward's rows).
+int stage_meta(tri_session* s, int which, const HostRows& R, const std::vector<int32_t>& sidx,
+               const std::vector<int32_t>& didx) {
+  if (s->meta_pending[which]) {
+    HIPCHK(hipEventSynchronize(s->meta_ev[which]));
+    s->meta_pending[which] = false;
+  }
   const MetaLayout ML = meta_layout(s->max_rows, s->max_batch);
   Meta h = meta_ptrs(s->hints, s->o_meta[which], ML);
   const size_t n = R.n();
@@ -290,12 +300,15 @@ void stage_meta(tri_session* s, int which, const HostRows& R, const std::vector<
     memcpy(h.sidx, sidx.data(), sidx.size() * 4);
     memcpy(h.didx, didx.data(), didx.size() * 4);
   }
+  return TRI_OK;
 }
 
 int upload_meta(tri_session* s, int which) {
   const MetaLayout ML = meta_layout(s->max_rows, s->max_batch);
   HIPCHK(hipMemcpyAsync(s->dints + s->o_meta[which], s->hints + s->o_meta[which], ML.size * 4,
                         hipMemcpyHostToDevice, s->st));
+  HIPCHK(hipEventRecord(s->meta_ev[which], s->st));
+  s->meta_pending[which] = true;
   return TRI_OK;
 }
 
@@ -324,7 +337,7 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
   int rc = prof_begin(s, PROF_FWD, &fslot);
   if (rc) return rc;
   const size_t layer_elems = (size_t)s->max_batch * s->css;
-  HIPCHK(launch_embed(dt, dm.tok, n, m->embed, D, s->x, s->st));
+  HIPCHK(launch_embed(dt, dm.tok, n, m->embed, d.vocab + 1, D, s->x, s->st));
   int prev_slots = 0;
   size_t prev_stride = 0;
   const float scale = 1.0f / std::sqrt((float)hd);
@@ -454,8 +467,8 @@ int step_ar(tri_session* s, const std::vector<int>& act, int stride, int32_t* ou
     last_row[j] = R.n() - 1;
     R.close_slot(act[j]);
   }
-  stage_meta(s, 0, R, {}, {});
-  int rc = upload_meta(s, 0);
+  int rc = stage_meta(s, 0, R, {}, {});
+  if (!rc) rc = upload_meta(s, 0);
   if (!rc) rc = forward(s, 0, R, s->logits);
   if (!rc) rc = sample(s, 0, R, s->logits, 0.f, 0);
   if (!rc) rc = d2h_ints(s, s->o_out_tok, R.n());
@@ -499,8 +512,8 @@ int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau
     }
     if (R.n() == 0) break;
     R.block_start.push_back(R.n());
-    stage_meta(s, 0, R, {}, {});
-    int rc = upload_meta(s, 0);
+    int rc = stage_meta(s, 0, R, {}, {});
+    if (!rc) rc = upload_meta(s, 0);
     if (!rc) rc = forward(s, 0, R, s->logits);
     if (!rc) rc = sample(s, 0, R, s->logits, tau, 0);
     if (!rc) rc = d2h_ints(s, s->o_out_tok, R.n());
@@ -571,11 +584,11 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
       d2.push_back((int32_t)(s->o_ars + j * (k + 1) + 1 + i));
     }
   }
-  stage_meta(s, 0, D, s1, d1);
-  stage_meta(s, 1, V, s2, d2);
   Meta m0 = meta_ptrs(s->dints, s->o_meta[0], ML);
   Meta m1 = meta_ptrs(s->dints, s->o_meta[1], ML);
-  int rc = upload_meta(s, 0);
+  int rc = stage_meta(s, 0, D, s1, d1);
+  if (!rc) rc = stage_meta(s, 1, V, s2, d2);
+  if (!rc) rc = upload_meta(s, 0);
   if (!rc) rc = upload_meta(s, 1);
   if (!rc) rc = forward(s, 0, D, s->logits);
   if (!rc) rc = sample(s, 0, D, s->logits, 0.f, 0);
@@ -585,6 +598,10 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
   for (size_t j = 0; j < na; ++j) {
     const Seq& S = s->seqs[act[j]];
     if (S.a_star < 0) continue;
+    if (s->meta_pending[1]) {  // the verify rows' host mirror is rewritten below
+      HIPCHK(hipEventSynchronize(s->meta_ev[1]));
+      s->meta_pending[1] = false;
+    }
     const int L = (int)S.tokens.size();
     int32_t* hd = s->hints + s->o_drafts + j * k;
     for (int i = 0; i < k; ++i) {
@@ -767,6 +784,15 @@ int tri_session_create(const tri_model* m, int max_batch, int max_ctx, int max_r
     return fail(TRI_EHIP, "hipHostMalloc: %s", hipGetErrorString(e));
   }
   memset(s->hints, 0, S.nints * 4);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&s->meta_ev[i], hipEventDisableTiming);
+  if (e != hipSuccess) {
+    for (int i = 0; i < 2; ++i)
+      if (s->meta_ev[i]) (void)hipEventDestroy(s->meta_ev[i]);
+    (void)hipHostFree(s->hints);
+    (void)hipHostFree(s->hconf);
+    delete s;
+    return fail(TRI_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+  }
   // RoPE table: angle pos * base^(-2i/hd) in double, stored as float cos/sin.
   const tri_model_desc& d = m->d;
   const int half = d.head_dim / 2;
@@ -781,6 +807,7 @@ int tri_session_create(const tri_model* m, int max_batch, int max_ctx, int max_r
   if (e == hipSuccess) e = hipMemcpyAsync(s->dints, s->hints, S.nints * 4, hipMemcpyHostToDevice, s->st);
   if (e == hipSuccess) e = hipStreamSynchronize(s->st);
   if (e != hipSuccess) {
+    for (hipEvent_t ev : s->meta_ev) (void)hipEventDestroy(ev);
     (void)hipHostFree(s->hints);
     (void)hipHostFree(s->hconf);
     delete s;
@@ -794,6 +821,8 @@ int tri_session_destroy(tri_session* s) {
   if (!s) return TRI_OK;
   (void)hipStreamSynchronize(s->st);
   for (hipEvent_t e : s->ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : s->meta_ev)
+    if (e) (void)hipEventDestroy(e);
   (void)hipHostFree(s->hints);
   (void)hipHostFree(s->hconf);
   delete s;
@@ -819,8 +848,8 @@ int tri_prefill(tri_session* s, int seq, const int32_t* tokens, int n) {
     HostRows R;
     for (int p = b; p < e; ++p) R.add(tokens[p], p, p + 1, seq, 0, 0);
     R.close_slot(seq);
-    stage_meta(s, 0, R, {}, {});
-    rc = upload_meta(s, 0);
+    rc = stage_meta(s, 0, R, {}, {});
+    if (!rc) rc = upload_meta(s, 0);
     if (!rc) rc = forward(s, 0, R, nullptr);
     if (rc) {
       S.active = false;
@@ -934,8 +963,8 @@ int tri_forward(tri_session* s, int n_rows, const int32_t* row_seq, const int32_
     if (sl == row_seq[n_rows - 1]) return fail(TRI_EINVAL, "rows of a sequence must be contiguous");
   R.close_slot(row_seq[n_rows - 1]);
   float* lg = logits ? logits : s->logits;
-  stage_meta(s, 0, R, {}, {});
-  int rc = upload_meta(s, 0);
+  int rc = stage_meta(s, 0, R, {}, {});
+  if (!rc) rc = upload_meta(s, 0);
   if (!rc) rc = forward(s, 0, R, lg);
   if (!rc) rc = sample(s, 0, R, lg, 0.f, 0);
   if (!rc) rc = d2h_ints(s, s->o_out_tok, n_rows);

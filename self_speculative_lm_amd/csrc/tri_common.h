@@ -73,8 +73,8 @@ size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split);
 hipError_t launch_attn(int dtype, const AttnLaunch& a, hipStream_t st);
 
 // Misc kernels.
-hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, int d, float* x,
-                        hipStream_t st);
+hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, int n_emb, int d,
+                        float* x, hipStream_t st);
 hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, size_t slot_stride,
                              int rows, int d, const float* g, float eps, void* y, hipStream_t st);
 hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t slot_stride, int rows,

@@ -149,6 +149,30 @@ def test_small_bf16_lora_lossless():
     assert err <= TOL_BF16, err
 
 
+@pytest.mark.parametrize("shape,plen,max_rows", [(seeded.TINY, 45, 8), (seeded.SMALL_BF16, 100, 16)])
+def test_prefill_in_many_chunks_matches_oracle(shape, plen, max_rows):
+    """A prompt longer than max_rows is prefilled in back-to-back chunks whose
+    metadata uploads are queued asynchronously (no tracing, so nothing
+    synchronises in between); the next step must see a correct cache."""
+    import self_speculative_lm_amd as tm
+    _, _, model, om = get(shape)
+    prompt = seeded.prompt(plen, shape.vocab, stream=7)
+    sess = tm.Session(model, max_batch=1, max_ctx=plen + 16, max_rows=max_rows)
+    sess.prefill(0, prompt)
+    sess.set_trace(True)
+    out, _ = sess.decode_step(tm.TRI_AR, 1)
+    tr = sess.trace()
+    o = OracleSession(om, plen + 16, prefill_chunk=max_rows)
+    o.prefill(prompt)
+    o.keep_logits = True
+    tok = o.ar_step()
+    err = float(np.abs(o.records[-1].logits - tr[-1]["logits"]).max())
+    tol = TOL_F32 if shape.dtype == "f32" else TOL_BF16
+    assert err <= tol, err
+    if top2_margin(o.records[-1].logits[-1]) > 2 * tol:
+        assert out[0, 0] == tok[0]
+
+
 def test_state_errors_and_kv_bookkeeping():
     import self_speculative_lm_amd as tm
     shape = seeded.TINY

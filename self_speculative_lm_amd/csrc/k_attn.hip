@@ -8,17 +8,19 @@
 // bf16 kernel (gfx950 MFMA): one workgroup per (split of kv_split keys,
 // group of up to 16*WAVES query vectors, sequence x kv head).  All query heads
 // of a kv head share the K/V tiles, so K [64 keys][128] and V^T [128][64 keys]
-// tiles are staged once in LDS (V is cached transposed, so both tiles are
-// contiguous 16-byte loads) and read by every wave.  Each wave owns 16 query
-// vectors and computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16: a lane then
-// holds 8 scores of one query for 8 consecutive keys (the K rows fed to the
-// MFMA are permuted so that this holds), so the softmax row statistics need
-// only two cross-lane steps, and the same registers, rounded to bf16, are
-// directly the B operand of O^T = V^T P^T -- no LDS round trip for P.
-// Online softmax in float32 (exp2 with the scale folded in).  Splits write
-// unnormalised partials (O, m, l) that a combine kernel merges in split order;
-// a launch with a single split normalises in place.  A row's result depends
-// only on its own q, its keys and kv_split, not on the other rows.
+// tiles are staged in LDS (V is cached transposed, so both tiles are
+// contiguous 16-byte loads) and read by every wave.  The tiles are
+// double-buffered: the loads of tile t+1 are in flight while tile t runs.
+// Each wave owns 16 query vectors and computes S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16.  The K rows fed to the MFMA are permuted so that a
+// lane ends up holding 8 scores of one query for 8 consecutive keys: the
+// softmax row statistics then need only two cross-lane steps, and the same
+// registers, rounded to bf16, are directly the B operand of O^T = V^T P^T (no
+// LDS round trip for P).  Online softmax in float32 (exp2 with the scale
+// folded in).  Splits write unnormalised partials (O, m, l) that a combine
+// kernel merges in split order; a launch with a single split normalises in
+// place.  A row's result depends only on its own q, its keys and kv_split,
+// not on the other rows of the launch.
 #include <math.h>
 
 #include "tri_common.h"
@@ -51,8 +53,11 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
 
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t ks[KT * KPAD];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[HD * VPAD];
+  constexpr int NT = WAVES * 64;
+  constexpr int PIECES = KT * HD / 8;  // 16-byte pieces of one K (or V^T) tile
+  constexpr int PPT = PIECES / NT;     // per thread
+  __shared__ __attribute__((aligned(16))) bf16_t ks[2][KT * KPAD];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[2][HD * VPAD];
   __shared__ int s_maxhi;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seq = blockIdx.z / a.hkv, kvh = blockIdx.z - seq * a.hkv;
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   {
     int myhi = 0;
     const int qend = min(nq, qbase + WAVES * 16);
-    for (int v = qbase + tid; v < qend; v += WAVES * 64) myhi = max(myhi, a.row_hi[r0 + v / G]);
+    for (int v = qbase + tid; v < qend; v += NT) myhi = max(myhi, a.row_hi[r0 + v / G]);
     atomicMax(&s_maxhi, myhi);
   }
   __syncthreads();
@@ -94,20 +99,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   const bf16_t* kbase = a.kc + (size_t)(cseq * a.hkv + kvh) * a.ctx * HD;
   const bf16_t* vbase = a.vc + (size_t)(cseq * a.hkv + kvh) * HD * a.ctx;
 
-  f32x4 oacc[8];
+  // Tile staging: registers <- global (keys >= kend read as zero), then LDS.
+  auto load_tile = [&](int t0, bf16x8* kr, bf16x8* vr) {
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -1e30f, l_run = 0.f;
-
-  for (int t0 = kbeg; t0 < kend; t0 += KT) {
-    for (int i = tid; i < KT * HD / 8; i += WAVES * 64) {
+    for (int u = 0; u < PPT; ++u) {
+      const int i = tid + u * NT;
       const int key = i >> 4, c = i & 15;
-      const bf16x8 val = (t0 + key < kend) ? ld16(kbase + (size_t)(t0 + key) * HD + c * 8) : zero;
-      *reinterpret_cast<bf16x8*>(&ks[key * KPAD + c * 8]) = val;
-    }
-    for (int i = tid; i < HD * KT / 8; i += WAVES * 64) {
-      const int d = i >> 3, c = i & 7;
-      const int key0 = t0 + c * 8;
+      kr[u] = (t0 + key < kend) ? ld16(kbase + (size_t)(t0 + key) * HD + c * 8) : zero;
+      const int d = i >> 3, c8 = i & 7;
+      const int key0 = t0 + c8 * 8;
       bf16x8 val = zero;
       if (key0 < kend) {
         val = ld16(vbase + (size_t)d * a.ctx + key0);
@@ -117,11 +117,27 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
             if (key0 + e >= kend) val[e] = (__bf16)0.0f;
         }
       }
-      *reinterpret_cast<bf16x8*>(&vs[d * VPAD + c * 8]) = val;
+      vr[u] = val;
     }
-    __syncthreads();
+  };
+  auto store_tile = [&](int b, const bf16x8* kr, const bf16x8* vr) {
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int i = tid + u * NT;
+      *reinterpret_cast<bf16x8*>(&ks[b][(i >> 4) * KPAD + (i & 15) * 8]) = kr[u];
+      *reinterpret_cast<bf16x8*>(&vs[b][(i >> 3) * VPAD + (i & 7) * 8]) = vr[u];
+    }
+  };
 
-    // S^T tiles: MFMA row i = 4*(j... see header) -> lane (j, g) gets keys 32m + 8g + e of query j
+  f32x4 oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+
+  // One 64-key tile from LDS buffer b starting at key t0.
+  auto compute = [&](int b, int t0) {
+    // S^T tile t of key group m: MFMA row i loads key 32m + 8(i/4) + 4t + i%4,
+    // so output lane (j, g) gets keys 32m + 8g + (4t + r) of query j.
     float p[2][8];
     float tmax = -INFINITY;
 #pragma unroll
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
         const int krow = 32 * m + 8 * (j >> 2) + 4 * t + (j & 3);
 #pragma unroll
         for (int ds = 0; ds < 4; ++ds) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[krow * KPAD + ds * 32 + g * 8]);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[b][krow * KPAD + ds * 32 + g * 8]);
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ds], s, 0, 0, 0);
         }
 #pragma unroll
@@ -167,11 +183,24 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[(16 * dt + j) * VPAD + 32 * m + 8 * g]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[b][(16 * dt + j) * VPAD + 32 * m + 8 * g]);
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[m], oacc[dt], 0, 0, 0);
       }
     }
+  };
+
+  bf16x8 kr[PPT], vr[PPT];
+  load_tile(kbeg, kr, vr);
+  store_tile(0, kr, vr);
+  __syncthreads();
+  int b = 0;
+  for (int t0 = kbeg; t0 < kend; t0 += KT) {
+    const bool more = t0 + KT < kend;
+    if (more) load_tile(t0 + KT, kr, vr);
+    compute(b, t0);
+    if (more) store_tile(b ^ 1, kr, vr);
     __syncthreads();
+    b ^= 1;
   }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -199,7 +228,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// Merge split partials of one (row, head) in split order.
+// Merge the split partials of one (row, head) in split order.
 template <typename T>
 __global__ void attn_combine_kernel(const float* part_o, const float* part_ml, const int32_t* row_hi,
                                     int rows, int hq, int hd, int kv_split, T* out) {
@@ -286,10 +315,9 @@ size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split) {
 hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   if (L.rows <= 0) return hipSuccess;
   if (dtype == TRI_F32) {
-    hipLaunchKernelGGL(attn_f32_kernel, dim3(L.rows, L.hq), dim3(64), 0, st,
-                       static_cast<const float*>(L.q), static_cast<const float*>(L.kc),
-                       static_cast<const float*>(L.vc), L.seq_start, L.slot_seq, L.n_seq, L.row_hi, L.hq, L.hkv,
-                       L.hd, L.ctx, L.scale, static_cast<float*>(L.out));
+    hipLaunchKernelGGL(attn_f32_kernel, dim3(L.rows, L.hq), dim3(64), 0, st, static_cast<const float*>(L.q),
+                       static_cast<const float*>(L.kc), static_cast<const float*>(L.vc), L.seq_start, L.slot_seq,
+                       L.n_seq, L.row_hi, L.hq, L.hkv, L.hd, L.ctx, L.scale, static_cast<float*>(L.out));
     return hipGetLastError();
   }
   AttnArgs a;
@@ -312,19 +340,17 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   a.part_ml = L.part + np * HD;
   const int G = L.hq / L.hkv;
   const int qtiles = (L.max_rows_per_seq * G + 15) / 16;
-  const int waves = qtiles >= 8 ? 8 : (qtiles >= 4 ? 4 : (qtiles >= 2 ? 2 : 1));
+  const int waves = qtiles > 4 ? 8 : 4;  // >= 4 waves: staging is spread over >= 256 threads
   const int qgroups = (qtiles + waves - 1) / waves;
   dim3 grid(a.nsplit, qgroups, L.n_seq * L.hkv);
-  switch (waves) {
-    case 1: hipLaunchKernelGGL(attn_bf16_kernel<1>, grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(attn_bf16_kernel<2>, grid, dim3(128), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(attn_bf16_kernel<8>, grid, dim3(512), 0, st, a); break;
-  }
+  if (waves == 4)
+    hipLaunchKernelGGL(attn_bf16_kernel<4>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<8>, grid, dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(L.rows, L.hq), dim3(HD), 0, st,
-                     a.part_o, a.part_ml, L.row_hi, L.rows, L.hq, HD, L.kv_split, a.out);
+  hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(L.rows, L.hq), dim3(HD), 0, st, a.part_o, a.part_ml,
+                     L.row_hi, L.rows, L.hq, HD, L.kv_split, a.out);
   return hipGetLastError();
 }
 

@@ -7,20 +7,23 @@
 // memory bound).  The bf16 path still runs the dot products on the matrix
 // cores (v_mfma_f32_16x16x32_bf16): a 16-feature x 16-row tile per MFMA, W as
 // the A operand read straight from global memory into registers (16 rows x 64
-// contiguous bytes per load instruction), the rows of X staged once per
-// workgroup in LDS in MFMA-fragment order (conflict-free 1 KiB reads) and
-// shared by the 4 waves.  Split-K across workgroups keeps >= ~512 workgroups in
-// flight for the N = 4096 projections; every split writes its own float32
-// partial slot and the consumer kernel (norm, RoPE, SwiGLU) adds the slots in
-// slot order, so results are deterministic and independent of M (a row's
-// value never depends on which other rows share the launch).
+// contiguous bytes per load instruction), the rows of X staged in LDS in
+// MFMA-fragment order (conflict-free 1 KiB reads) and shared by the waves of
+// the workgroup.  Both are double-buffered over 256-wide K chunks: the loads
+// of chunk c+1 are in flight while chunk c runs on the matrix cores.
+// Split-K across workgroups keeps enough workgroups in flight for the N = d
+// projections; every split writes its own float32 partial slot and the
+// consumer kernel (norm, RoPE, SwiGLU) adds the slots in slot order, so results
+// are deterministic and independent of M (a row's value never depends on which
+// other rows share the launch).
 #include "tri_common.h"
 
 namespace tri {
 namespace {
 
-constexpr int KC = 256;          // K per LDS stage
+constexpr int KC = 256;          // K per stage
 constexpr int KSTEPS = KC / 32;  // MFMA k-steps per stage
+constexpr int MAX_S = 16;        // split-K slots (a LoRA slot may be added by the caller)
 
 struct GemmArgs {
   const bf16_t* X;
@@ -38,16 +41,20 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Grid: x = N/64 feature blocks, y = K splits, z = 16*MT-row tiles of X.
-// Wave w of a workgroup owns features [64*x + 16*w, +16).
-template <int MT>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ bf16x8 xs[KSTEPS][MT][64];
+// Grid: x = feature blocks of 16*WAVES, y = K splits, z = 16*MT-row tiles of X.
+// Wave w of a workgroup owns features [16*WAVES*x + 16*w, +16).
+template <int MT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int NT = WAVES * 64;
+  constexpr int XPIECES = MT * 16 * (KC / 8);     // 16-byte pieces of one X chunk
+  constexpr int XPT = (XPIECES + NT - 1) / NT;    // pieces per thread
+  __shared__ bf16x8 xs[2][KSTEPS][MT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int n0 = blockIdx.x * (16 * WAVES) + wave * 16;
   const int m0 = blockIdx.z * (MT * 16);
   const int kbeg = blockIdx.y * a.Ks;
   const int kend = min(a.K, kbeg + a.Ks);
+  const int nch = (kend - kbeg + KC - 1) / KC;
 
   // Segment of this wave's features (segment boundaries are multiples of 64;
   // rows past the end of the last segment are clamped and never stored).
@@ -66,35 +73,70 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   const int wr = min(nl + (lane & 15), sr - 1);
   // A operand: lane l supplies W[n0 + l%16][k + 8*(l/16) .. +8]
   const bf16_t* wrow = wb + (size_t)wr * a.K + (lane >> 4) * 8;
-
-  f32x4 acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero = {};
 
-  for (int kc = kbeg; kc < kend; kc += KC) {
-    bf16x8 wf[KSTEPS];
+  auto load_w = [&](int kc, bf16x8* wf) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const int k = kc + s * 32;
       wf[s] = (k < kend) ? ld16(wrow + k) : zero;
     }
-    // B operand staging: xs[s][t][g*16 + j] = X[m0 + 16t + j][kc + 32s + 8g .. +8]
+  };
+  // B operand staging: xs[b][s][t][g*16 + j] = X[m0 + 16t + j][kc + 32s + 8g .. +8]
+  auto load_x = [&](int kc, bf16x8* xr) {
 #pragma unroll
-    for (int it = 0; it < 2 * MT; ++it) {
-      const int i = tid + it * 256;
+    for (int it = 0; it < XPT; ++it) {
+      const int i = tid + it * NT;
       const int g = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
       const int k = kc + s * 32 + g * 8, m = m0 + r;
-      xs[s][r >> 4][g * 16 + (r & 15)] =
-          (m < a.M && k < kend) ? ld16(a.X + (size_t)m * a.K + k) : zero;
+      xr[it] = (i < XPIECES && m < a.M && k < kend) ? ld16(a.X + (size_t)m * a.K + k) : zero;
     }
-    __syncthreads();
+  };
+  auto store_x = [&](int b, const bf16x8* xr) {
+#pragma unroll
+    for (int it = 0; it < XPT; ++it) {
+      const int i = tid + it * NT;
+      if (i < XPIECES) {
+        const int g = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
+        xs[b][s][r >> 4][g * 16 + (r & 15)] = xr[it];
+      }
+    }
+  };
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int b, const bf16x8* wf) {
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
       for (int t = 0; t < MT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s], xs[s][t][lane], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s], xs[b][s][t][lane], acc[t], 0, 0, 0);
     }
+  };
+
+  bf16x8 wA[KSTEPS], wB[KSTEPS], xr[XPT];
+  load_w(kbeg, wA);
+  load_x(kbeg, xr);
+  store_x(0, xr);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    const bool h1 = c + 1 < nch;
+    if (h1) {
+      load_w(kbeg + (c + 1) * KC, wB);
+      load_x(kbeg + (c + 1) * KC, xr);
+    }
+    compute(0, wA);
+    if (h1) store_x(1, xr);
+    __syncthreads();
+    if (!h1) break;
+    const bool h2 = c + 2 < nch;
+    if (h2) {
+      load_w(kbeg + (c + 2) * KC, wA);
+      load_x(kbeg + (c + 2) * KC, xr);
+    }
+    compute(1, wB);
+    if (h2) store_x(0, xr);
     __syncthreads();
   }
   // D layout: lane l holds D[4*(l/16) + r][l%16] = Y[m0 + 16t + l%16][n0 + 4*(l/16) + r]
@@ -137,25 +179,51 @@ __global__ __launch_bounds__(64) void gemm_f32_kernel(const float* X, int M, int
   P[(size_t)m * N + n] = acc;
 }
 
+template <int MT>
+void launch_mt(const GemmArgs& a, const GemmPlan& p, int M, hipStream_t st) {
+  const int fb = 16 * p.waves;
+  const dim3 grid((a.N + fb - 1) / fb, p.S, (M + 16 * MT - 1) / (16 * MT));
+  if (p.waves == 8)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, 8>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, 4>), grid, dim3(256), 0, st, a);
+}
+
 }  // namespace
 
+// The plan depends only on (N, K), never on M, so that a row's result is the
+// same whatever the number of rows in the launch.
 GemmPlan gemm_plan(int N, int K, int dtype) {
   GemmPlan p;
+  p.waves = 4;
   if (dtype != TRI_BF16) {
     p.S = 1;
     p.Ks = K;
     return p;
   }
-  const int nblk = (N + 63) / 64;
-  int S = (768 + nblk / 2) / (nblk > 0 ? nblk : 1);
-  const int maxS = K / KC > 0 ? K / KC : 1;
-  if (S < 1) S = 1;
-  if (S > maxS) S = maxS;
-  int Ks = (K + S - 1) / S;
+  // Measured on MI355X for the 8B/14B decode shapes (M = 32/33): 8-wave
+  // workgroups everywhere; K per split about 512 for the d x d and QKV
+  // projections, 768 for the long-K down projection, 1024 for the wide
+  // gate/up projection; the lm_head (very wide N) runs unsplit.
+  p.waves = N >= 128 ? 8 : 4;
+  int Ks;
+  if (N >= 65536)
+    Ks = K;
+  else if (N >= 16384)
+    Ks = 1024;
+  else if (K > 8192)
+    Ks = 768;
+  else
+    Ks = 512;
   Ks = (Ks + KC - 1) / KC * KC;
   if (Ks > K) Ks = (K + 31) / 32 * 32;
+  int S = (K + Ks - 1) / Ks;
+  if (S > MAX_S) {
+    Ks = ((K + MAX_S - 1) / MAX_S + KC - 1) / KC * KC;  // fewer, longer splits
+    S = (K + Ks - 1) / Ks;
+  }
   p.Ks = Ks;
-  p.S = (K + Ks - 1) / Ks;
+  p.S = S;
   return p;
 }
 
@@ -184,12 +252,11 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const WSeg* segs,
     a.P = P;
     a.slot_stride = slot_stride;
     const int mt = M >= 64 ? 4 : (M + 15) / 16;
-    dim3 grid((N + 63) / 64, plan.S, (M + 16 * mt - 1) / (16 * mt));
     switch (mt) {
-      case 1: hipLaunchKernelGGL(gemm_bf16_kernel<1>, grid, dim3(256), 0, st, a); break;
-      case 2: hipLaunchKernelGGL(gemm_bf16_kernel<2>, grid, dim3(256), 0, st, a); break;
-      case 3: hipLaunchKernelGGL(gemm_bf16_kernel<3>, grid, dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL(gemm_bf16_kernel<4>, grid, dim3(256), 0, st, a); break;
+      case 1: launch_mt<1>(a, plan, M, st); break;
+      case 2: launch_mt<2>(a, plan, M, st); break;
+      case 3: launch_mt<3>(a, plan, M, st); break;
+      default: launch_mt<4>(a, plan, M, st); break;
     }
   } else {
     dim3 grid((N + 63) / 64, M);

@@ -10,20 +10,42 @@
 namespace tri {
 namespace {
 
-// Sum of the partial slots of column c of row r (slot order).
+constexpr int MAX_SLOTS = 17;  // split-K partial slots a consumer adds (<= 16 GEMM splits + a LoRA slot)
+
+// Sum of the partial slots at offset `off` (slot order).  All slot loads are
+// issued before the first add so their latencies overlap.
 __device__ __forceinline__ float slot_sum(const float* P, int nslots, size_t stride, size_t off) {
-  float acc = P[off];
-  for (int s = 1; s < nslots; ++s) acc += P[s * stride + off];
+  float v[MAX_SLOTS];
+#pragma unroll
+  for (int s = 0; s < MAX_SLOTS; ++s) v[s] = s < nslots ? P[s * stride + off] : 0.f;
+  float acc = v[0];
+#pragma unroll
+  for (int s = 1; s < MAX_SLOTS; ++s)
+    if (s < nslots) acc += v[s];
   return acc;
 }
 
-// Fixed-order block sum over 256 threads.
-__device__ float block_sum_256(float v, float* red) {
+// The same for four consecutive columns (off % 4 == 0, stride % 4 == 0).
+__device__ __forceinline__ f32x4 slot_sum4(const float* P, int nslots, size_t stride, size_t off) {
+  f32x4 v[MAX_SLOTS];
+#pragma unroll
+  for (int s = 0; s < MAX_SLOTS; ++s)
+    v[s] = s < nslots ? *reinterpret_cast<const f32x4*>(P + s * stride + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int s = 1; s < MAX_SLOTS; ++s)
+    if (s < nslots) acc += v[s];
+  return acc;
+}
+
+// Fixed-order sum over the blockDim.x (a multiple of 64, <= 1024) threads.
+__device__ float block_sum(float v, float* red) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  const float t = (red[0] + red[1]) + (red[2] + red[3]);
+  float t = red[0];
+  for (int w = 1; w < nw; ++w) t += red[w];
   __syncthreads();
   return t;
 }
@@ -40,60 +62,60 @@ __global__ void embed_kernel(const int32_t* tok, const T* E, int n_emb, int d, f
 }
 
 // x[r] += sum of slots; y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g   (RMSNorm).
-constexpr int NORM_VPT = 32;  // d <= 256 * 32
+// One 1024-thread workgroup per row, four columns per thread per pass.
+constexpr int NORM_THREADS = 1024;
+constexpr int NORM_VPT = 2;  // float4 groups per thread: d <= 1024 * 4 * 2
 template <typename T>
-__global__ __launch_bounds__(256) void resid_norm_kernel(float* x, const float* P, int nslots,
-                                                         size_t stride, int d, const float* g,
-                                                         float eps, T* y) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* x, const float* P, int nslots,
+                                                                  size_t stride, int d, const float* g,
+                                                                  float eps, T* y) {
+  __shared__ float red[NORM_THREADS / 64];
   const int r = blockIdx.x, tid = threadIdx.x;
   float* xr = x + (size_t)r * d;
-  float v[NORM_VPT];
+  f32x4 v[NORM_VPT];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NORM_VPT; ++i) {
-    const int c = tid + i * 256;
-    float val = 0.f;
+    const int c = (tid + i * NORM_THREADS) * 4;
+    f32x4 val = {0.f, 0.f, 0.f, 0.f};
     if (c < d) {
-      val = xr[c];
+      val = *reinterpret_cast<const f32x4*>(xr + c);
       if (nslots > 0) {
-        val += slot_sum(P, nslots, stride, (size_t)r * d + c);
-        xr[c] = val;
+        val += slot_sum4(P, nslots, stride, (size_t)r * d + c);
+        *reinterpret_cast<f32x4*>(xr + c) = val;
       }
     }
     v[i] = val;
-    ss += val * val;
+    ss += val[0] * val[0] + val[1] * val[1] + val[2] * val[2] + val[3] * val[3];
   }
-  const float tot = block_sum_256(ss, red);
+  const float tot = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int i = 0; i < NORM_VPT; ++i) {
-    const int c = tid + i * 256;
-    if (c < d) Elem<T>::store(y, (size_t)r * d + c, v[i] * inv * g[c]);
+    const int c = (tid + i * NORM_THREADS) * 4;
+    if (c < d)
+      for (int e = 0; e < 4; ++e) Elem<T>::store(y, (size_t)r * d + c + e, v[i][e] * inv * g[c + e]);
   }
 }
 
 // Sum the QKV slots, rotate q and k (rotate-half pairs (i, i + hd/2) by
 // pos * base^(-2i/hd), cos/sin table precomputed), store q and write k, v
 // into the cache slot of the row's position (V transposed).
+// Grid (rows, hq + 2*hkv heads), one wave per (row, head): q and k heads
+// rotate pairs (c, c + hd/2), v heads are copied to the transposed V cache.
 template <typename T>
-__global__ __launch_bounds__(256) void rope_kv_kernel(const float* P, int nslots, size_t stride, int hq,
-                                                      int hkv, int hd, const int32_t* row_seq,
-                                                      const int32_t* row_pos, const float* rope,
-                                                      T* qout, T* kc, T* vc, int ctx, size_t css) {
-  const int r = blockIdx.x;
+__global__ __launch_bounds__(64) void rope_kv_kernel(const float* P, int nslots, size_t stride, int hq,
+                                                     int hkv, int hd, const int32_t* row_seq,
+                                                     const int32_t* row_pos, const float* rope,
+                                                     T* qout, T* kc, T* vc, int ctx, size_t css) {
+  const int r = blockIdx.x, h = blockIdx.y;
   const int pos = row_pos[r], seq = row_seq[r];
   const int half = hd / 2;
-  const int N = (hq + 2 * hkv) * hd;
-  const size_t rb = (size_t)r * N;
-  const int npair = (hq + hkv) * half;
-  const int total = npair + hkv * hd;
-  for (int i = threadIdx.x; i < total; i += blockDim.x) {
-    if (i < npair) {
-      const int h = i / half, c = i - h * half;
-      const int ca = h * hd + c;
-      const float xa = slot_sum(P, nslots, stride, rb + ca);
-      const float xb = slot_sum(P, nslots, stride, rb + ca + half);
+  const size_t rb = (size_t)r * (hq + 2 * hkv) * hd + (size_t)h * hd;
+  if (h < hq + hkv) {
+    for (int c = threadIdx.x; c < half; c += 64) {
+      const float xa = slot_sum(P, nslots, stride, rb + c);
+      const float xb = slot_sum(P, nslots, stride, rb + c + half);
       const float cs = rope[((size_t)pos * half + c) * 2];
       const float sn = rope[((size_t)pos * half + c) * 2 + 1];
       const float ra = xa * cs - xb * sn;
@@ -107,25 +129,30 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* P, int nslots
         Elem<T>::store(kc, o, ra);
         Elem<T>::store(kc, o + half, rbv);
       }
-    } else {
-      const int vi = i - npair;
-      const int kh = vi / hd, dd = vi - kh * hd;
-      const float val = slot_sum(P, nslots, stride, rb + (size_t)(hq + hkv) * hd + vi);
+    }
+  } else {
+    const int kh = h - hq - hkv;
+    for (int dd = threadIdx.x; dd < hd; dd += 64) {
+      const float val = slot_sum(P, nslots, stride, rb + dd);
       Elem<T>::store(vc, (size_t)seq * css + ((size_t)kh * hd + dd) * ctx + pos, val);
     }
   }
 }
 
-// h = silu(gate) * up with gate = slots of columns [0, ffn), up = [ffn, 2 ffn).
+// h = silu(gate) * up with gate = slots of columns [0, ffn), up = [ffn, 2 ffn);
+// one thread per four consecutive columns of one row.
 template <typename T>
-__global__ void swiglu_kernel(const float* P, int nslots, size_t stride, int ffn, T* h) {
-  const int r = blockIdx.x;
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* P, int nslots, size_t stride, int rows,
+                                                     int ffn, T* h) {
+  const int q4 = ffn / 4;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * q4) return;
+  const int r = i / q4, c = (i - r * q4) * 4;
   const size_t rb = (size_t)r * 2 * ffn;
-  for (int c = threadIdx.x; c < ffn; c += blockDim.x) {
-    const float gt = slot_sum(P, nslots, stride, rb + c);
-    const float up = slot_sum(P, nslots, stride, rb + ffn + c);
-    Elem<T>::store(h, (size_t)r * ffn + c, gt / (1.0f + expf(-gt)) * up);
-  }
+  const f32x4 gt = slot_sum4(P, nslots, stride, rb + c);
+  const f32x4 up = slot_sum4(P, nslots, stride, rb + ffn + c);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Elem<T>::store(h, (size_t)r * ffn + c + e, gt[e] / (1.0f + expf(-gt[e])) * up[e]);
 }
 
 // LoRA middle activation A o, kept only on flagged rows (zero elsewhere).
@@ -310,11 +337,11 @@ hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, 
 hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, size_t stride, int rows,
                              int d, const float* g, float eps, void* y, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (d > 256 * NORM_VPT) return hipErrorInvalidValue;
+  if (d > NORM_THREADS * 4 * NORM_VPT || d % 4 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
   TRI_DISPATCH(dtype,
-               hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(rows), dim3(256), 0, st, x, P, nslots,
+               hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(rows), dim3(NORM_THREADS), 0, st, x, P, nslots,
                                   stride, d, g, eps, static_cast<float*>(y)),
-               hipLaunchKernelGGL(resid_norm_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, x, P,
+               hipLaunchKernelGGL(resid_norm_kernel<bf16_t>, dim3(rows), dim3(NORM_THREADS), 0, st, x, P,
                                   nslots, stride, d, g, eps, static_cast<bf16_t*>(y)));
   return hipGetLastError();
 }
@@ -323,11 +350,13 @@ hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, 
                           int hd, const int32_t* row_seq, const int32_t* row_pos, const float* rope,
                           void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  const dim3 grid(rows, hq + 2 * hkv);
   TRI_DISPATCH(dtype,
-               hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(rows), dim3(256), 0, st, P, nslots, stride,
+               hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(64), 0, st, P, nslots, stride,
                                   hq, hkv, hd, row_seq, row_pos, rope, static_cast<float*>(qout),
                                   static_cast<float*>(kc), static_cast<float*>(vc), ctx, css),
-               hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, P, nslots,
+               hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(64), 0, st, P, nslots,
                                   stride, hq, hkv, hd, row_seq, row_pos, rope,
                                   static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
                                   static_cast<bf16_t*>(vc), ctx, css));
@@ -337,10 +366,12 @@ hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, 
 hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t stride, int rows, int ffn, void* h,
                          hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (ffn % 4 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(((size_t)rows * (ffn / 4) + 255) / 256));
   TRI_DISPATCH(dtype,
-               hipLaunchKernelGGL(swiglu_kernel<float>, dim3(rows), dim3(256), 0, st, P, nslots, stride,
+               hipLaunchKernelGGL(swiglu_kernel<float>, grid, dim3(256), 0, st, P, nslots, stride, rows,
                                   ffn, static_cast<float*>(h)),
-               hipLaunchKernelGGL(swiglu_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, P, nslots, stride,
+               hipLaunchKernelGGL(swiglu_kernel<bf16_t>, grid, dim3(256), 0, st, P, nslots, stride, rows,
                                   ffn, static_cast<bf16_t*>(h)));
   return hipGetLastError();
 }

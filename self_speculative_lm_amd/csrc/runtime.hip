@@ -708,7 +708,7 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   m->p_o = gemm_plan(d.d_model, qd, d.dtype);
   m->p_gu = gemm_plan(2 * d.d_ffn, d.d_model, d.dtype);
   m->p_down = gemm_plan(d.d_model, d.d_ffn, d.dtype);
-  m->p_lm = GemmPlan{1, d.d_model};
+  m->p_lm = GemmPlan{1, d.d_model, d.vocab >= 8192 ? 8 : 4};
   m->p_la = d.lora_rank > 0 ? gemm_plan(d.lora_rank, qd, d.dtype) : GemmPlan{1, qd};
   m->p_lb = d.lora_rank > 0 ? GemmPlan{1, d.lora_rank} : GemmPlan{0, 0};
   *out = m;

@@ -47,8 +47,9 @@ struct WSeg {
   int rows;
 };
 struct GemmPlan {
-  int S;   // K splits
-  int Ks;  // K per split (multiple of 32)
+  int S;          // K splits
+  int Ks;         // K per split (multiple of 32)
+  int waves = 4;  // waves per workgroup (16 features each)
 };
 GemmPlan gemm_plan(int N, int K, int dtype);
 hipError_t launch_gemm(int dtype, const void* X, int M, int K, const WSeg* segs, int nseg, int N,

@@ -124,6 +124,8 @@ def main():
     log(f"weights ready in {time.time() - t0:.1f}s")
     model = tm.Model(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn,
                      shape.vocab, tensors, dtype=tm.TRI_BF16)
+    del tensors  # the model holds its own packed copy
+    torch.cuda.empty_cache()
     max_ctx = args.prompt + (k + 1) * (args.steps + args.warmup + 2) + 64
     sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=128, device=dev)
     prompt = seeded.prompt(args.prompt, shape.vocab)
@@ -220,7 +222,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        del sess, model, tensors
+        del sess, model
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(shape, args.prompt, k, tpr)
     print(json.dumps(result), flush=True)

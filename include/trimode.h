@@ -87,12 +87,18 @@ const char* tri_last_error(void);
  *   final_norm [d] (float32), lm_head [vocab][d]
  *   if lora_rank > 0, per layer l: lora_a [r][hq*hd], lora_b [d][r]
  * so n_weights = 1 + 9*n_layers + 2 + (lora_rank > 0 ? 2*n_layers : 0).
- * The model keeps the pointers: the weights must stay alive and unchanged
- * until tri_model_destroy.  bf16 models need d, hq*hd, hkv*hd, ffn and r to be
- * multiples of 64 and head_dim == 128; float32 models need head_dim <= 128.
+ * tri_model_create copies the embedding and norm gains into model_buf (caller
+ * allocated device memory of tri_model_bytes bytes, 256-byte aligned) and
+ * repacks every projection matrix there in the order the GEMM kernel streams
+ * it (bf16: MFMA-fragment order).  It runs on `stream` and returns after the
+ * copies are done: the caller may then free the original weights; model_buf
+ * must stay alive and unchanged until tri_model_destroy.  bf16 models need d,
+ * hq*hd, hkv*hd, ffn and r to be multiples of 64 and head_dim == 128; float32
+ * models need head_dim <= 128; d and ffn are multiples of 4, d <= 8192.
  * ------------------------------------------------------------------------ */
+int tri_model_bytes(const tri_model_desc* desc, size_t* bytes);
 int tri_model_create(const tri_model_desc* desc, const void* const* weights, int n_weights,
-                     tri_model** out);
+                     void* model_buf, size_t bytes, void* stream, tri_model** out);
 int tri_model_destroy(tri_model* model);
 
 /* ------------------------------------------------------------------------

@@ -56,19 +56,27 @@ def weight_names(n_layers: int, lora_rank: int = 0) -> List[str]:
 
 
 class Model:
-    """tri_model over caller-owned device weight tensors (kept alive here)."""
+    """tri_model: the weights are copied/repacked into a torch-allocated model
+    buffer (kept here); the caller's weight tensors may be dropped afterwards."""
 
     def __init__(self, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab, weights,
-                 dtype: int = TRI_BF16, rope_base: float = 10000.0, rms_eps: float = 1e-6, lora_rank: int = 0):
+                 dtype: int = TRI_BF16, rope_base: float = 10000.0, rms_eps: float = 1e-6, lora_rank: int = 0,
+                 stream=None):
+        torch = _torch()
         names = weight_names(n_layers, lora_rank)
         if isinstance(weights, dict):
             weights = [weights[n] for n in names]
-        self.weights = list(weights)
+        weights = list(weights)
         self.desc = ModelDesc(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab, rope_base, rms_eps,
                               dtype, lora_rank)
-        arr = (ctypes.c_void_p * len(self.weights))(*[w.data_ptr() for w in self.weights])
+        n = ctypes.c_size_t()
+        check(lib().tri_model_bytes(ctypes.byref(self.desc), ctypes.byref(n)))
+        self.buffer = torch.empty(n.value + 256, dtype=torch.uint8, device=weights[0].device)
+        off = (-self.buffer.data_ptr()) % 256
+        arr = (ctypes.c_void_p * len(weights))(*[w.data_ptr() for w in weights])
         h = ctypes.c_void_p()
-        check(lib().tri_model_create(ctypes.byref(self.desc), arr, len(self.weights), ctypes.byref(h)))
+        check(lib().tri_model_create(ctypes.byref(self.desc), arr, len(weights), self.buffer.data_ptr() + off,
+                                     n.value, _stream(stream), ctypes.byref(h)))
         self.handle = h
         self.vocab = vocab
 

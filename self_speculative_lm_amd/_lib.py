@@ -41,7 +41,8 @@ FP = ctypes.POINTER(ctypes.c_float)
 # name -> (restype, argtypes); every exported symbol of the header
 SIGNATURES = {
     "tri_last_error": (ctypes.c_char_p, []),
-    "tri_model_create": (I, [ctypes.POINTER(ModelDesc), ctypes.POINTER(P), I, ctypes.POINTER(P)]),
+    "tri_model_bytes": (I, [ctypes.POINTER(ModelDesc), ctypes.POINTER(SZ)]),
+    "tri_model_create": (I, [ctypes.POINTER(ModelDesc), ctypes.POINTER(P), I, P, SZ, P, ctypes.POINTER(P)]),
     "tri_model_destroy": (I, [P]),
     "tri_session_bytes": (I, [P, I, I, I, ctypes.POINTER(SZ)]),
     "tri_session_create": (I, [P, I, I, I, P, SZ, P, ctypes.POINTER(P)]),

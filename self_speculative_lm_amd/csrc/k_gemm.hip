@@ -4,18 +4,28 @@
 // At decode shapes M is 1..64 rows per 64-row tile while N*K is the whole
 // weight matrix, so the kernel is bound by streaming W from HBM (every weight
 // is loaded once per forward: [Blog], the paragraph on why AR decoding is
-// memory bound).  The bf16 path still runs the dot products on the matrix
-// cores (v_mfma_f32_16x16x32_bf16): a 16-feature x 16-row tile per MFMA, W as
-// the A operand read straight from global memory into registers (16 rows x 64
-// contiguous bytes per load instruction), the rows of X staged in LDS in
-// MFMA-fragment order (conflict-free 1 KiB reads) and shared by the waves of
-// the workgroup.  Both are double-buffered over 256-wide K chunks: the loads
-// of chunk c+1 are in flight while chunk c runs on the matrix cores.
+// memory bound).  The bf16 path runs the dot products on the matrix cores
+// (v_mfma_f32_16x16x32_bf16: 16 features x 16 rows x 32 k per instruction).
+//
+// Weight layout.  At model creation every bf16 projection matrix is repacked
+// once into MFMA-fragment order: the A operand of one MFMA (16 rows x 32 k,
+// lane l holding row l%16, k-octet l/16) is one contiguous 1 KiB block, the 8
+// fragments of a 128-row group at one k-step are adjacent, and k-steps follow
+// each other.  A wave's load instruction therefore reads 1 KiB contiguous, a
+// workgroup's K chunk is one contiguous block, and the whole matrix is swept
+// almost linearly, in exactly the register layout the MFMA consumes.
+//
+// X rows are staged in LDS in fragment order (conflict-free 1 KiB reads) and
+// shared by the 8 waves; W registers and X tiles are double-buffered over
+// 256-wide K chunks so the loads of chunk c+1 are in flight while chunk c runs.
 // Split-K across workgroups keeps enough workgroups in flight for the N = d
 // projections; every split writes its own float32 partial slot and the
 // consumer kernel (norm, RoPE, SwiGLU) adds the slots in slot order, so results
 // are deterministic and independent of M (a row's value never depends on which
 // other rows share the launch).
+#include <algorithm>
+#include <cstdlib>
+
 #include "tri_common.h"
 
 namespace tri {
@@ -24,15 +34,19 @@ namespace {
 constexpr int KC = 256;          // K per stage
 constexpr int KSTEPS = KC / 32;  // MFMA k-steps per stage
 constexpr int MAX_S = 16;        // split-K slots (a LoRA slot may be added by the caller)
+constexpr int WAVES_PER_WG = 8;  // waves per gemm workgroup, 16 features each
+constexpr int GROUP = 16 * WAVES_PER_WG;  // rows per packing group (one workgroup's features)
+
+// K is padded with zero weights to a whole number of stages in the packed
+// layout, so every stage of every split is full.
+__host__ __device__ __forceinline__ int kpad(int K) { return (K + KC - 1) / KC * KC; }
 
 struct GemmArgs {
   const bf16_t* X;
-  int M, K;
-  const bf16_t* w0;
-  const bf16_t* w1;
-  const bf16_t* w2;
-  int r0, r1, r2;  // rows of the segments (0 = absent)
-  int N, Ks;
+  int M, K, Kp;  // Kp = kpad(K)
+  const bf16_t* W;  // packed
+  int N, Ks, S;
+  int nfb, ntiles;  // feature blocks; tiles = (M tiles) x nfb x S
   float* P;
   size_t slot_stride;
 };
@@ -41,107 +55,147 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Grid: x = feature blocks of 16*WAVES, y = K splits, z = 16*MT-row tiles of X.
-// Wave w of a workgroup owns features [16*WAVES*x + 16*w, +16).
-template <int MT, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int NT = WAVES * 64;
-  constexpr int XPIECES = MT * 16 * (KC / 8);     // 16-byte pieces of one X chunk
-  constexpr int XPT = (XPIECES + NT - 1) / NT;    // pieces per thread
+// Packed element offset of fragment (row tile i, k-step s) for kpad(K)/32 = ks32 k-steps.
+__host__ __device__ __forceinline__ size_t frag_offset(int i, int s, int ks32) {
+  return ((((size_t)(i >> 3) * ks32 + s) << 3) + (i & 7)) * 512;
+}
+
+// Repack W (up to three row segments, row-major [rows][K]) into fragment
+// order; rows past N and columns past K are zero.  One thread per 16-byte piece.
+__global__ void pack_bf16_kernel(const bf16_t* w0, const bf16_t* w1, const bf16_t* w2, int r0, int r1, int N,
+                                 int K, size_t npieces, bf16_t* dst) {
+  const int ks32 = kpad(K) / 32;
+  for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < npieces;
+       p += (size_t)gridDim.x * blockDim.x) {
+    const size_t f = p >> 6;
+    const int lane = (int)(p & 63);
+    const int i_in = (int)(f & 7);
+    const size_t gs = f >> 3;
+    const int s = (int)(gs % ks32);
+    const int grp = (int)(gs / ks32);
+    const int row = (grp * 8 + i_in) * 16 + (lane & 15);
+    const int k = s * 32 + (lane >> 4) * 8;
+    bf16x8 v = {};
+    if (row < N && k < K) {
+      const bf16_t* src;
+      if (row < r0)
+        src = w0 + (size_t)row * K;
+      else if (row < r0 + r1)
+        src = w1 + (size_t)(row - r0) * K;
+      else
+        src = w2 + (size_t)(row - r0 - r1) * K;
+      v = ld16(src + k);
+    }
+    *reinterpret_cast<bf16x8*>(dst + p * 8) = v;
+  }
+}
+
+// float32 models keep row-major weights: the segments are concatenated.
+__global__ void pack_f32_kernel(const float* w0, const float* w1, const float* w2, int r0, int r1, int N, int K,
+                                float* dst) {
+  const size_t n = (size_t)N * K;
+  for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < n; p += (size_t)gridDim.x * blockDim.x) {
+    const int row = (int)(p / K);
+    const size_t c = p - (size_t)row * K;
+    const float* src = row < r0 ? w0 + (size_t)row * K
+                                : (row < r0 + r1 ? w1 + (size_t)(row - r0) * K : w2 + (size_t)(row - r0 - r1) * K);
+    dst[p] = src[c];
+  }
+}
+
+// One workgroup per tile t = (M tile z, K split y, feature block x), x
+// fastest.  Wave w of a workgroup owns row tile i = x*WAVES + w (features
+// [16i, 16i+16)) and writes it to the split's partial slot.
+//
+// A split is processed in passes of NCH stages of KC = 256 k.  Every pass is
+// straight-line code (NCH is a template argument and the stage loop is fully
+// unrolled): the W fragments of stage c+1 are in flight while stage c
+// multiplies, X is double-buffered in LDS, and each stage issues its X loads
+// before its W loads so that staging X waits for those loads only.  Every
+// stage is full (K is padded with zero weights) and rows past M read a
+// clamped row whose results are never stored, so no load is conditional.
+//
+// No W fragment is carried across a loop back-edge: with a runtime stage loop
+// (fragments kept in registers from one iteration to the next) this compiler
+// reused the upper half of a live 16x16x32 MFMA operand for other values, a
+// miscompile that the operand check over the built assembly detects.
+template <int MT, int NCH>
+__global__ __launch_bounds__(WAVES_PER_WG * 64) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int WAVES = WAVES_PER_WG, NT = WAVES * 64;
+  constexpr int XPIECES = MT * 16 * (KC / 8);  // 16-byte pieces of one X stage
+  constexpr int XPT = XPIECES / NT;             // pieces per thread
+  static_assert(XPIECES % NT == 0, "every thread stages the same number of X pieces");
   __shared__ bf16x8 xs[2][KSTEPS][MT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * (16 * WAVES) + wave * 16;
-  const int m0 = blockIdx.z * (MT * 16);
-  const int kbeg = blockIdx.y * a.Ks;
-  const int kend = min(a.K, kbeg + a.Ks);
-  const int nch = (kend - kbeg + KC - 1) / KC;
+  const int fbx = blockIdx.x % a.nfb;
+  const int rest = blockIdx.x / a.nfb;
+  const int y = rest % a.S;
+  const int m0 = (rest / a.S) * (MT * 16);
+  const int tile = fbx * WAVES + wave;
+  const int kbeg = y * a.Ks;
+  const int npass = (min(a.Kp, kbeg + a.Ks) - kbeg) / (NCH * KC);
+  const bf16_t* wt0 = a.W + frag_offset(tile, kbeg >> 5, a.Kp / 32) + lane * 8;
 
-  // Segment of this wave's features (segment boundaries are multiples of 64;
-  // rows past the end of the last segment are clamped and never stored).
-  const bf16_t* wb = a.w0;
-  int nl = n0, sr = a.r0;
-  if (nl >= a.r0 && a.r1 > 0) {
-    nl -= a.r0;
-    wb = a.w1;
-    sr = a.r1;
-    if (nl >= a.r1 && a.r2 > 0) {
-      nl -= a.r1;
-      wb = a.w2;
-      sr = a.r2;
-    }
+  // B operand staging: xs[b][s][t][g*16 + j] = X[m0 + 16t + j][k + 32s + 8g .. +8]
+  const bf16_t* xrow[XPT];
+  int xk[XPT];
+#pragma unroll
+  for (int it = 0; it < XPT; ++it) {
+    const int i = tid + it * NT;
+    const int g = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
+    xrow[it] = a.X + (size_t)min(m0 + r, a.M - 1) * a.K;
+    xk[it] = s * 32 + g * 8;
   }
-  const int wr = min(nl + (lane & 15), sr - 1);
-  // A operand: lane l supplies W[n0 + l%16][k + 8*(l/16) .. +8]
-  const bf16_t* wrow = wb + (size_t)wr * a.K + (lane >> 4) * 8;
-  const bf16x8 zero = {};
-
-  auto load_w = [&](int kc, bf16x8* wf) {
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const int k = kc + s * 32;
-      wf[s] = (k < kend) ? ld16(wrow + k) : zero;
-    }
-  };
-  // B operand staging: xs[b][s][t][g*16 + j] = X[m0 + 16t + j][kc + 32s + 8g .. +8]
-  auto load_x = [&](int kc, bf16x8* xr) {
-#pragma unroll
-    for (int it = 0; it < XPT; ++it) {
-      const int i = tid + it * NT;
-      const int g = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
-      const int k = kc + s * 32 + g * 8, m = m0 + r;
-      xr[it] = (i < XPIECES && m < a.M && k < kend) ? ld16(a.X + (size_t)m * a.K + k) : zero;
-    }
-  };
-  auto store_x = [&](int b, const bf16x8* xr) {
-#pragma unroll
-    for (int it = 0; it < XPT; ++it) {
-      const int i = tid + it * NT;
-      if (i < XPIECES) {
-        const int g = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
-        xs[b][s][r >> 4][g * 16 + (r & 15)] = xr[it];
-      }
-    }
-  };
-
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int b, const bf16x8* wf) {
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s], xs[b][s][t][lane], acc[t], 0, 0, 0);
-    }
-  };
 
-  bf16x8 wA[KSTEPS], wB[KSTEPS], xr[XPT];
-  load_w(kbeg, wA);
-  load_x(kbeg, xr);
-  store_x(0, xr);
-  __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    const bool h1 = c + 1 < nch;
-    if (h1) {
-      load_w(kbeg + (c + 1) * KC, wB);
-      load_x(kbeg + (c + 1) * KC, xr);
-    }
-    compute(0, wA);
-    if (h1) store_x(1, xr);
+  for (int p = 0; p < npass; ++p) {
+    const int k0 = kbeg + p * (NCH * KC);
+    const bf16_t* wt = wt0 + (size_t)p * NCH * (KSTEPS * 8 * 512);
+    bf16x8 w[2][KSTEPS], xr[XPT];
+    auto load_x = [&](int c) {
+#pragma unroll
+      for (int it = 0; it < XPT; ++it)
+        xr[it] = ld16(xrow[it] + min(k0 + c * KC + xk[it], a.K - 8));  // padded K: zero weights there
+    };
+    auto load_w = [&](int c, bf16x8* wf) {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) wf[s] = ld16(wt + (size_t)(c * KSTEPS + s) * (8 * 512));
+    };
+    auto store_x = [&](int b) {
+#pragma unroll
+      for (int it = 0; it < XPT; ++it) {
+        const int i = tid + it * NT;
+        const int g = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
+        xs[b][s][r >> 4][g * 16 + (r & 15)] = xr[it];
+      }
+    };
+    if (p > 0) __syncthreads();  // the previous pass's last stage still reads xs
+    load_x(0);
+    load_w(0, w[0]);
+    store_x(0);
     __syncthreads();
-    if (!h1) break;
-    const bool h2 = c + 2 < nch;
-    if (h2) {
-      load_w(kbeg + (c + 2) * KC, wA);
-      load_x(kbeg + (c + 2) * KC, xr);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (c + 1 < NCH) {
+        load_x(c + 1);
+        load_w(c + 1, w[(c + 1) & 1]);
+      }
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[c & 1][s], xs[c & 1][s][t][lane], acc[t], 0, 0, 0);
+      if (c + 1 < NCH) {
+        store_x((c + 1) & 1);
+        __syncthreads();
+      }
     }
-    compute(1, wB);
-    if (h2) store_x(0, xr);
-    __syncthreads();
   }
   // D layout: lane l holds D[4*(l/16) + r][l%16] = Y[m0 + 16t + l%16][n0 + 4*(l/16) + r]
-  float* out = a.P + (size_t)blockIdx.y * a.slot_stride;
-  const int nn = n0 + 4 * (lane >> 4);
+  float* out = a.P + (size_t)y * a.slot_stride;
+  const int nn = tile * 16 + 4 * (lane >> 4);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = m0 + t * 16 + (lane & 15);
@@ -156,113 +210,146 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // float32 path (small models): one thread per output, sequential K order.
-__global__ __launch_bounds__(64) void gemm_f32_kernel(const float* X, int M, int K, const float* w0,
-                                                       const float* w1, const float* w2, int r0,
-                                                       int r1, int N, float* P) {
+__global__ __launch_bounds__(64) void gemm_f32_kernel(const float* X, int M, int K, const float* W, int N,
+                                                       float* P) {
   const int n = blockIdx.x * 64 + threadIdx.x;
   const int m = blockIdx.y;
   if (n >= N || m >= M) return;
-  const float* wb;
-  int nl = n;
-  if (nl < r0) {
-    wb = w0;
-  } else if ((nl -= r0) < r1) {
-    wb = w1;
-  } else {
-    nl -= r1;
-    wb = w2;
-  }
-  const float* wr = wb + (size_t)nl * K;
+  const float* wr = W + (size_t)n * K;
   const float* xr = X + (size_t)m * K;
   float acc = 0.f;
   for (int k = 0; k < K; ++k) acc = fmaf(xr[k], wr[k], acc);
   P[(size_t)m * N + n] = acc;
 }
 
+template <int MT, int NCH>
+void launch_tiles(const GemmArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<MT, NCH>), dim3(a.ntiles), dim3(WAVES_PER_WG * 64), 0, st, a);
+}
+
 template <int MT>
-void launch_mt(const GemmArgs& a, const GemmPlan& p, int M, hipStream_t st) {
-  const int fb = 16 * p.waves;
-  const dim3 grid((a.N + fb - 1) / fb, p.S, (M + 16 * MT - 1) / (16 * MT));
-  if (p.waves == 8)
-    hipLaunchKernelGGL((gemm_bf16_kernel<MT, 8>), grid, dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<MT, 4>), grid, dim3(256), 0, st, a);
+hipError_t launch_mt(GemmArgs a, const GemmPlan& p, int M, hipStream_t st) {
+  a.nfb = (a.N + 16 * WAVES_PER_WG - 1) / (16 * WAVES_PER_WG);
+  a.S = p.S;
+  a.ntiles = a.nfb * p.S * ((M + 16 * MT - 1) / (16 * MT));
+  switch (p.nch) {
+    case 1: launch_tiles<MT, 1>(a, st); break;
+    case 2: launch_tiles<MT, 2>(a, st); break;
+    case 3: launch_tiles<MT, 3>(a, st); break;
+    case 4: launch_tiles<MT, 4>(a, st); break;
+    case 5: launch_tiles<MT, 5>(a, st); break;
+    case 6: launch_tiles<MT, 6>(a, st); break;
+    case 8: launch_tiles<MT, 8>(a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
 // The plan depends only on (N, K), never on M, so that a row's result is the
 // same whatever the number of rows in the launch.
-GemmPlan gemm_plan(int N, int K, int dtype) {
+GemmPlan gemm_plan(int N, int K, int dtype, bool unsplit) {
   GemmPlan p;
-  p.waves = 4;
   if (dtype != TRI_BF16) {
     p.S = 1;
     p.Ks = K;
+    p.nch = 1;
     return p;
   }
-  // Measured on MI355X for the 8B/14B decode shapes (M = 32/33): 8-wave
-  // workgroups everywhere; K per split about 512 for the d x d and QKV
-  // projections, 768 for the long-K down projection, 1024 for the wide
-  // gate/up projection; the lm_head (very wide N) runs unsplit.
-  p.waves = N >= 128 ? 8 : 4;
-  int Ks;
-  if (N >= 65536)
-    Ks = K;
-  else if (N >= 16384)
-    Ks = 1024;
+  // Target K per split, measured on MI355X for the 8B/14B decode shapes
+  // (M = 32/33) with one workgroup per (128-feature block, K split): 512 for
+  // the d x d projection, 1024 for QKV and the wide gate/up projection, 1536
+  // for the long-K down projection; the lm_head (very wide N) runs unsplit.
+  const int T = kpad(K) / KC;  // stages of the padded K
+  int tgt;
+  if (unsplit || N >= 65536)
+    tgt = T;
   else if (K > 8192)
-    Ks = 768;
+    tgt = 1536 / KC;
+  else if (N > K)
+    tgt = 1024 / KC;
   else
-    Ks = 512;
-  Ks = (Ks + KC - 1) / KC * KC;
-  if (Ks > K) Ks = (K + 31) / 32 * 32;
-  int S = (K + Ks - 1) / Ks;
-  if (S > MAX_S) {
-    Ks = ((K + MAX_S - 1) / MAX_S + KC - 1) / KC * KC;  // fewer, longer splits
-    S = (K + Ks - 1) / Ks;
+    tgt = 512 / KC;
+  tgt = std::max(1, std::min(tgt, T));
+  // Prefer a split count that divides the stages evenly, within a factor of
+  // two of the target; otherwise the last split is shorter.
+  const int S0 = std::min((T + tgt - 1) / tgt, MAX_S);
+  int S = 0;
+  for (int d = 0; d <= S0 && !S; ++d)
+    for (int c : {S0 + d, S0 - d})
+      if (!S && c >= 1 && c <= MAX_S && c <= 2 * S0 && 2 * c >= S0 && T % c == 0) S = c;
+  if (!S) S = S0;
+  const int ps = (T + S - 1) / S;  // stages per split
+  p.S = (T + ps - 1) / ps;
+  p.Ks = ps * KC;
+  const int last = T - (p.S - 1) * ps;
+  int g = ps;  // gcd(ps, last): a pass length that divides both split lengths
+  for (int b = last; b;) {
+    const int t = g % b;
+    g = b;
+    b = t;
   }
-  p.Ks = Ks;
-  p.S = S;
+  p.nch = 1;
+  for (int c : {8, 6, 5, 4, 3, 2})
+    if (g % c == 0) {
+      p.nch = c;
+      break;
+    }
   return p;
 }
 
-hipError_t launch_gemm(int dtype, const void* X, int M, int K, const WSeg* segs, int nseg, int N,
-                       const GemmPlan& plan, float* P, size_t slot_stride, hipStream_t st) {
+size_t gemm_packed_bytes(int N, int K, int dtype) {
+  if (dtype == TRI_BF16) return (size_t)((N + GROUP - 1) / GROUP) * GROUP * kpad(K) * 2;
+  return (size_t)N * K * 4;
+}
+
+hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, void* dst, hipStream_t st) {
   const void* w0 = segs[0].ptr;
   const void* w1 = nseg > 1 ? segs[1].ptr : nullptr;
   const void* w2 = nseg > 2 ? segs[2].ptr : nullptr;
   const int r0 = segs[0].rows;
   const int r1 = nseg > 1 ? segs[1].rows : 0;
-  const int r2 = nseg > 2 ? segs[2].rows : 0;
+  if (dtype == TRI_BF16) {
+    const size_t npieces = gemm_packed_bytes(N, K, dtype) / 16;
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(2048), dim3(256), 0, st, static_cast<const bf16_t*>(w0),
+                       static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w2), r0, r1, N, K, npieces,
+                       static_cast<bf16_t*>(dst));
+  } else {
+    hipLaunchKernelGGL(pack_f32_kernel, dim3(2048), dim3(256), 0, st, static_cast<const float*>(w0),
+                       static_cast<const float*>(w1), static_cast<const float*>(w2), r0, r1, N, K,
+                       static_cast<float*>(dst));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, int N, const GemmPlan& plan, float* P,
+                       size_t slot_stride, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (dtype == TRI_BF16) {
     GemmArgs a;
     a.X = static_cast<const bf16_t*>(X);
     a.M = M;
     a.K = K;
-    a.w0 = static_cast<const bf16_t*>(w0);
-    a.w1 = static_cast<const bf16_t*>(w1);
-    a.w2 = static_cast<const bf16_t*>(w2);
-    a.r0 = r0;
-    a.r1 = r1;
-    a.r2 = r2;
+    a.Kp = kpad(K);
+    a.W = static_cast<const bf16_t*>(W);
     a.N = N;
     a.Ks = plan.Ks;
     a.P = P;
     a.slot_stride = slot_stride;
     const int mt = M >= 64 ? 4 : (M + 15) / 16;
+    hipError_t e;
     switch (mt) {
-      case 1: launch_mt<1>(a, plan, M, st); break;
-      case 2: launch_mt<2>(a, plan, M, st); break;
-      case 3: launch_mt<3>(a, plan, M, st); break;
-      default: launch_mt<4>(a, plan, M, st); break;
+      case 1: e = launch_mt<1>(a, plan, M, st); break;
+      case 2: e = launch_mt<2>(a, plan, M, st); break;
+      case 3: e = launch_mt<3>(a, plan, M, st); break;
+      default: e = launch_mt<4>(a, plan, M, st); break;
     }
+    if (e != hipSuccess) return e;
   } else {
     dim3 grid((N + 63) / 64, M);
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(64), 0, st, static_cast<const float*>(X), M, K,
-                       static_cast<const float*>(w0), static_cast<const float*>(w1),
-                       static_cast<const float*>(w2), r0, r1, N, P);
+                       static_cast<const float*>(W), N, P);
   }
   return hipGetLastError();
 }

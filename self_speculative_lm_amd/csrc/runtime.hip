@@ -43,8 +43,9 @@ int fail(int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// One layer's weights inside the model buffer (projections packed for the GEMM).
 struct Layer {
-  const void *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+  const void *qkv, *o, *gu, *down;
   const float *n1, *n2;
   const void *la, *lb;
 };
@@ -347,9 +348,8 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
     char* vc = s->vbuf + l * layer_elems * m->esz;
     HIPCHK(launch_resid_norm(dt, s->x, s->part, prev_slots, prev_stride, n, D, L.n1, d.rms_eps, s->ybuf, s->st));
     {
-      WSeg segs[3] = {{L.wq, qd}, {L.wk, hkv * hd}, {L.wv, hkv * hd}};
       const size_t stride = (size_t)n * m->qkv_n;
-      PROF(PROF_QKV, launch_gemm(dt, s->ybuf, n, D, segs, 3, m->qkv_n, m->p_qkv, s->part, stride, s->st));
+      PROF(PROF_QKV, launch_gemm(dt, s->ybuf, n, D, L.qkv, m->qkv_n, m->p_qkv, s->part, stride, s->st));
       HIPCHK(launch_rope_kv(dt, s->part, m->p_qkv.S, stride, n, hq, hkv, hd, dm.seq, dm.pos, s->rope, s->qbuf, kc,
                             vc, s->ctx, s->css, s->st));
     }
@@ -378,38 +378,32 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
     int oslots = m->p_o.S;
     const size_t ostride = (size_t)n * D;
     {
-      WSeg seg = {L.wo, D};
-      PROF(PROF_O, launch_gemm(dt, s->abuf, n, qd, &seg, 1, D, m->p_o, s->part, ostride, s->st));
+      PROF(PROF_O, launch_gemm(dt, s->abuf, n, qd, L.o, D, m->p_o, s->part, ostride, s->st));
     }
     if (any_lora) {
       const int rk = d.lora_rank;
-      WSeg sa = {L.la, rk};
       const size_t astride = (size_t)n * rk;
-      HIPCHK(launch_gemm(dt, s->abuf, n, qd, &sa, 1, rk, m->p_la, s->part2, astride, s->st));
+      HIPCHK(launch_gemm(dt, s->abuf, n, qd, L.la, rk, m->p_la, s->part2, astride, s->st));
       HIPCHK(launch_lora_mid(dt, s->part2, m->p_la.S, astride, n, rk, dm.lora, s->ybuf, s->st));
-      WSeg sb = {L.lb, D};
-      HIPCHK(launch_gemm(dt, s->ybuf, n, rk, &sb, 1, D, m->p_lb, s->part + (size_t)oslots * ostride, ostride, s->st));
+      HIPCHK(launch_gemm(dt, s->ybuf, n, rk, L.lb, D, m->p_lb, s->part + (size_t)oslots * ostride, ostride, s->st));
       oslots += m->p_lb.S;
     }
     HIPCHK(launch_resid_norm(dt, s->x, s->part, oslots, ostride, n, D, L.n2, d.rms_eps, s->ybuf, s->st));
     {
-      WSeg segs[2] = {{L.wg, d.d_ffn}, {L.wu, d.d_ffn}};
       const size_t stride = (size_t)n * 2 * d.d_ffn;
-      PROF(PROF_GU, launch_gemm(dt, s->ybuf, n, D, segs, 2, 2 * d.d_ffn, m->p_gu, s->part, stride, s->st));
+      PROF(PROF_GU, launch_gemm(dt, s->ybuf, n, D, L.gu, 2 * d.d_ffn, m->p_gu, s->part, stride, s->st));
       HIPCHK(launch_swiglu(dt, s->part, m->p_gu.S, stride, n, d.d_ffn, s->ybuf, s->st));
     }
     {
-      WSeg seg = {L.wd, D};
       prev_stride = (size_t)n * D;
-      PROF(PROF_DOWN, launch_gemm(dt, s->ybuf, n, d.d_ffn, &seg, 1, D, m->p_down, s->part, prev_stride, s->st));
+      PROF(PROF_DOWN, launch_gemm(dt, s->ybuf, n, d.d_ffn, L.down, D, m->p_down, s->part, prev_stride, s->st));
       prev_slots = m->p_down.S;
     }
   }
   if (logits_out) {
     HIPCHK(launch_resid_norm(dt, s->x, s->part, prev_slots, prev_stride, n, D, m->final_norm, d.rms_eps, s->ybuf,
                              s->st));
-    WSeg seg = {m->lm_head, d.vocab};
-    PROF(PROF_LM, launch_gemm(dt, s->ybuf, n, D, &seg, 1, d.vocab, m->p_lm, logits_out, (size_t)n * d.vocab, s->st));
+    PROF(PROF_LM, launch_gemm(dt, s->ybuf, n, D, m->lm_head, d.vocab, m->p_lm, logits_out, (size_t)n * d.vocab, s->st));
   }
   rc = prof_end(s, PROF_FWD, fslot);
   if (rc) return rc;
@@ -652,15 +646,18 @@ extern "C" {
 
 const char* tri_last_error(void) { return g_err.c_str(); }
 
-int tri_model_create(const tri_model_desc* desc, const void* const* weights, int n_weights, tri_model** out) {
-  if (!desc || !weights || !out) return fail(TRI_EINVAL, "null argument");
-  const tri_model_desc& d = *desc;
+}  // extern "C"
+
+namespace {
+
+int validate_desc(const tri_model_desc& d) {
   if (d.n_layers <= 0 || d.d_model <= 0 || d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.head_dim <= 0 ||
       d.d_ffn <= 0 || d.vocab <= 0 || d.lora_rank < 0)
     return fail(TRI_EINVAL, "non-positive model dimension");
   if (d.n_q_heads % d.n_kv_heads) return fail(TRI_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
   if (d.head_dim % 2) return fail(TRI_EINVAL, "head_dim must be even");
-  if (d.d_model > 8192) return fail(TRI_EINVAL, "d_model > 8192 not supported");
+  if (d.d_model > 8192 || d.d_model % 4) return fail(TRI_EINVAL, "d_model must be a multiple of 4, <= 8192");
+  if (d.d_ffn % 4) return fail(TRI_EINVAL, "d_ffn must be a multiple of 4");
   if (!(d.rms_eps > 0) || !(d.rope_base > 1)) return fail(TRI_EINVAL, "bad rms_eps/rope_base");
   if (d.dtype == TRI_BF16) {
     if (d.head_dim != 128) return fail(TRI_EINVAL, "bf16 models need head_dim == 128");
@@ -672,45 +669,135 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   } else {
     return fail(TRI_EINVAL, "bad dtype %d", d.dtype);
   }
+  return TRI_OK;
+}
+
+// Offsets of everything the model keeps in its buffer.
+struct ModelLayout {
+  struct L {
+    size_t qkv, o, gu, down, n1, n2, la, lb;
+  };
+  size_t embed, final_norm, lm_head, total;
+  std::vector<L> layers;
+};
+
+ModelLayout model_layout(const tri_model_desc& d) {
+  ModelLayout M;
+  const size_t esz = d.dtype == TRI_BF16 ? 2 : 4;
+  const int qd = d.n_q_heads * d.head_dim, kd = d.n_kv_heads * d.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = off;
+    off = align256(off + bytes);
+    return r;
+  };
+  M.embed = take((size_t)(d.vocab + 1) * d.d_model * esz);
+  M.layers.resize(d.n_layers);
+  for (auto& L : M.layers) {
+    L.qkv = take(gemm_packed_bytes(qd + 2 * kd, d.d_model, d.dtype));
+    L.o = take(gemm_packed_bytes(d.d_model, qd, d.dtype));
+    L.gu = take(gemm_packed_bytes(2 * d.d_ffn, d.d_model, d.dtype));
+    L.down = take(gemm_packed_bytes(d.d_model, d.d_ffn, d.dtype));
+    L.n1 = take((size_t)d.d_model * 4);
+    L.n2 = take((size_t)d.d_model * 4);
+    L.la = d.lora_rank > 0 ? take(gemm_packed_bytes(d.lora_rank, qd, d.dtype)) : 0;
+    L.lb = d.lora_rank > 0 ? take(gemm_packed_bytes(d.d_model, d.lora_rank, d.dtype)) : 0;
+  }
+  M.final_norm = take((size_t)d.d_model * 4);
+  M.lm_head = take(gemm_packed_bytes(d.vocab, d.d_model, d.dtype));
+  M.total = off;
+  return M;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tri_model_bytes(const tri_model_desc* desc, size_t* bytes) {
+  if (!desc || !bytes) return fail(TRI_EINVAL, "null argument");
+  int rc = validate_desc(*desc);
+  if (rc) return rc;
+  *bytes = model_layout(*desc).total;
+  return TRI_OK;
+}
+
+int tri_model_create(const tri_model_desc* desc, const void* const* weights, int n_weights, void* model_buf,
+                     size_t bytes, void* stream, tri_model** out) {
+  if (!desc || !weights || !out || !model_buf) return fail(TRI_EINVAL, "null argument");
+  const tri_model_desc& d = *desc;
+  int rc = validate_desc(d);
+  if (rc) return rc;
   const int expect = 1 + 9 * d.n_layers + 2 + (d.lora_rank > 0 ? 2 * d.n_layers : 0);
   if (n_weights != expect) return fail(TRI_EINVAL, "expected %d weight pointers, got %d", expect, n_weights);
   for (int i = 0; i < n_weights; ++i)
     if (!weights[i]) return fail(TRI_EINVAL, "weight pointer %d is null", i);
-  tri_model* m = new tri_model();
-  m->d = d;
-  m->esz = d.dtype == TRI_BF16 ? 2 : 4;
+  const ModelLayout ML = model_layout(d);
+  if (bytes < ML.total) return fail(TRI_ECAPACITY, "model buffer has %zu bytes, needs %zu", bytes, ML.total);
+  if (reinterpret_cast<uintptr_t>(model_buf) & 255) return fail(TRI_EINVAL, "model buffer must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(model_buf);
+  const size_t esz = d.dtype == TRI_BF16 ? 2 : 4;
+  const int qd = d.n_q_heads * d.head_dim, kd = d.n_kv_heads * d.head_dim;
+  const int dt = d.dtype;
+  // Copy the embedding and norm gains, repack every projection matrix.
   int w = 0;
-  m->embed = weights[w++];
-  m->layers.resize(d.n_layers);
+  HIPCHK(hipMemcpyAsync(base + ML.embed, weights[w++], (size_t)(d.vocab + 1) * d.d_model * esz,
+                        hipMemcpyDeviceToDevice, st));
+  std::vector<int> la_idx(d.n_layers), lb_idx(d.n_layers);
   for (int l = 0; l < d.n_layers; ++l) {
-    Layer& L = m->layers[l];
-    L.wq = weights[w++];
-    L.wk = weights[w++];
-    L.wv = weights[w++];
-    L.wo = weights[w++];
-    L.wg = weights[w++];
-    L.wu = weights[w++];
-    L.wd = weights[w++];
-    L.n1 = static_cast<const float*>(weights[w++]);
-    L.n2 = static_cast<const float*>(weights[w++]);
-    L.la = L.lb = nullptr;
+    const ModelLayout::L& L = ML.layers[l];
+    WSeg qkv[3] = {{weights[w], qd}, {weights[w + 1], kd}, {weights[w + 2], kd}};
+    HIPCHK(launch_pack(dt, qkv, 3, qd + 2 * kd, d.d_model, base + L.qkv, st));
+    WSeg o = {weights[w + 3], d.d_model};
+    HIPCHK(launch_pack(dt, &o, 1, d.d_model, qd, base + L.o, st));
+    WSeg gu[2] = {{weights[w + 4], d.d_ffn}, {weights[w + 5], d.d_ffn}};
+    HIPCHK(launch_pack(dt, gu, 2, 2 * d.d_ffn, d.d_model, base + L.gu, st));
+    WSeg dn = {weights[w + 6], d.d_model};
+    HIPCHK(launch_pack(dt, &dn, 1, d.d_model, d.d_ffn, base + L.down, st));
+    HIPCHK(hipMemcpyAsync(base + L.n1, weights[w + 7], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(base + L.n2, weights[w + 8], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
+    w += 9;
   }
-  m->final_norm = static_cast<const float*>(weights[w++]);
-  m->lm_head = weights[w++];
+  HIPCHK(hipMemcpyAsync(base + ML.final_norm, weights[w++], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
+  {
+    WSeg lm = {weights[w++], d.vocab};
+    HIPCHK(launch_pack(dt, &lm, 1, d.vocab, d.d_model, base + ML.lm_head, st));
+  }
   if (d.lora_rank > 0)
     for (int l = 0; l < d.n_layers; ++l) {
-      m->layers[l].la = weights[w++];
-      m->layers[l].lb = weights[w++];
+      WSeg a = {weights[w++], d.lora_rank};
+      HIPCHK(launch_pack(dt, &a, 1, d.lora_rank, qd, base + ML.layers[l].la, st));
+      WSeg b = {weights[w++], d.d_model};
+      HIPCHK(launch_pack(dt, &b, 1, d.d_model, d.lora_rank, base + ML.layers[l].lb, st));
     }
-  const int qd = d.n_q_heads * d.head_dim;
-  m->qkv_n = qd + 2 * d.n_kv_heads * d.head_dim;
+  HIPCHK(hipStreamSynchronize(st));
+  tri_model* m = new tri_model();
+  m->d = d;
+  m->esz = esz;
+  m->embed = base + ML.embed;
+  m->layers.resize(d.n_layers);
+  for (int l = 0; l < d.n_layers; ++l) {
+    const ModelLayout::L& L = ML.layers[l];
+    Layer& Y = m->layers[l];
+    Y.qkv = base + L.qkv;
+    Y.o = base + L.o;
+    Y.gu = base + L.gu;
+    Y.down = base + L.down;
+    Y.n1 = reinterpret_cast<const float*>(base + L.n1);
+    Y.n2 = reinterpret_cast<const float*>(base + L.n2);
+    Y.la = d.lora_rank > 0 ? base + L.la : nullptr;
+    Y.lb = d.lora_rank > 0 ? base + L.lb : nullptr;
+  }
+  m->final_norm = reinterpret_cast<const float*>(base + ML.final_norm);
+  m->lm_head = base + ML.lm_head;
+  m->qkv_n = qd + 2 * kd;
   m->p_qkv = gemm_plan(m->qkv_n, d.d_model, d.dtype);
   m->p_o = gemm_plan(d.d_model, qd, d.dtype);
   m->p_gu = gemm_plan(2 * d.d_ffn, d.d_model, d.dtype);
   m->p_down = gemm_plan(d.d_model, d.d_ffn, d.dtype);
-  m->p_lm = GemmPlan{1, d.d_model, d.vocab >= 8192 ? 8 : 4};
+  m->p_lm = gemm_plan(d.vocab, d.d_model, d.dtype, /*unsplit=*/true);
   m->p_la = d.lora_rank > 0 ? gemm_plan(d.lora_rank, qd, d.dtype) : GemmPlan{1, qd};
-  m->p_lb = d.lora_rank > 0 ? GemmPlan{1, d.lora_rank} : GemmPlan{0, 0};
+  m->p_lb = d.lora_rank > 0 ? gemm_plan(d.d_model, d.lora_rank, d.dtype) : GemmPlan{0, 0};
   *out = m;
   return TRI_OK;
 }

@@ -47,13 +47,19 @@ struct WSeg {
   int rows;
 };
 struct GemmPlan {
-  int S;          // K splits
-  int Ks;         // K per split (multiple of 32)
-  int waves = 4;  // waves per workgroup (16 features each)
+  int S;        // K splits (partial slots)
+  int Ks;       // K per split (bf16: a multiple of the 256-wide stage)
+  int nch = 1;  // bf16: stages per straight-line pass (divides every split's stages)
 };
-GemmPlan gemm_plan(int N, int K, int dtype);
-hipError_t launch_gemm(int dtype, const void* X, int M, int K, const WSeg* segs, int nseg, int N,
-                       const GemmPlan& plan, float* P, size_t slot_stride, hipStream_t st);
+// unsplit: one K split whatever the shape (the lm_head writes logits directly).
+GemmPlan gemm_plan(int N, int K, int dtype, bool unsplit = false);
+// Bytes of a packed weight matrix (bf16: MFMA-fragment order, rows padded to
+// 128; float32: row-major) and the packing launch (segments concatenated).
+size_t gemm_packed_bytes(int N, int K, int dtype);
+hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, void* dst, hipStream_t st);
+// Y = X W^T with W packed by launch_pack.
+hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, int N, const GemmPlan& plan,
+                       float* P, size_t slot_stride, hipStream_t st);
 
 struct AttnLaunch {
   const void* q;

@@ -51,36 +51,45 @@ def _desc(**kw):
     return ModelDesc(**d)
 
 
-def _create(L, desc, n=None, null_at=None):
+def _create(L, desc, n=None, null_at=None, buf=0x100000, nbytes=1 << 40):
     n_w = 1 + 9 * desc.n_layers + 2 + (2 * desc.n_layers if desc.lora_rank else 0)
     ptrs = [0x1000 * (i + 1) for i in range(n_w if n is None else n)]
     if null_at is not None:
         ptrs[null_at] = 0
     arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
     h = ctypes.c_void_p()
-    rc = L.tri_model_create(ctypes.byref(desc), arr, len(ptrs), ctypes.byref(h))
-    return rc, h
+    return L.tri_model_create(ctypes.byref(desc), arr, len(ptrs), buf, nbytes, None, ctypes.byref(h))
 
 
-def test_model_create_validates_on_host(L):
-    from self_speculative_lm_amd._lib import TRI_EINVAL, TRI_F32
-    rc, h = _create(L, _desc())
-    assert rc == 0
+def _bytes(L, desc):
     n = ctypes.c_size_t()
-    assert L.tri_session_bytes(h, 1, 1000, 64, ctypes.byref(n)) == 0
-    assert n.value > 0
-    big = ctypes.c_size_t()
-    assert L.tri_session_bytes(h, 2, 1000, 64, ctypes.byref(big)) == 0
-    assert big.value > n.value            # a second sequence adds a KV cache
-    assert L.tri_session_bytes(h, 0, 1000, 64, ctypes.byref(n)) == TRI_EINVAL
-    assert L.tri_model_destroy(h) == 0
-    assert _create(L, _desc(head_dim=64))[0] == TRI_EINVAL          # bf16 needs hd 128
-    assert _create(L, _desc(n_q_heads=3))[0] == TRI_EINVAL          # hq % hkv
-    assert _create(L, _desc(), n=5)[0] == TRI_EINVAL                # pointer count
-    assert _create(L, _desc(), null_at=3)[0] == TRI_EINVAL          # null weight
-    assert _create(L, _desc(dtype=7))[0] == TRI_EINVAL
-    assert _create(L, _desc(dtype=TRI_F32, head_dim=32, d_model=128, n_q_heads=4, n_kv_heads=4))[0] == 0
-    assert b"weight" in L.tri_last_error() or len(L.tri_last_error()) >= 0
+    rc = L.tri_model_bytes(ctypes.byref(desc), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_model_descriptor_and_buffer_validation_on_host(L):
+    from self_speculative_lm_amd._lib import TRI_ECAPACITY, TRI_EINVAL, TRI_F32
+    rc, small = _bytes(L, _desc())
+    assert rc == 0 and small > 0
+    rc, more = _bytes(L, _desc(n_layers=3))
+    assert rc == 0 and more > small                          # one more layer of weights
+    rc, lora = _bytes(L, _desc(lora_rank=64))
+    assert rc == 0 and lora > small                          # the adapter is stored too
+    # bf16 projection rows are padded to 128 in the packed layout
+    rc, b1 = _bytes(L, _desc(vocab=1000))
+    rc2, b2 = _bytes(L, _desc(vocab=1024))
+    assert rc == rc2 == 0 and b1 <= b2
+    assert _bytes(L, _desc(head_dim=64))[0] == TRI_EINVAL    # bf16 needs hd 128
+    assert _bytes(L, _desc(n_q_heads=3))[0] == TRI_EINVAL    # hq % hkv
+    assert _bytes(L, _desc(dtype=7))[0] == TRI_EINVAL
+    assert _bytes(L, _desc(dtype=TRI_F32, head_dim=32, d_model=128, n_q_heads=4, n_kv_heads=4))[0] == 0
+    # creation is refused before any device work for bad pointers and buffers
+    assert _create(L, _desc(), n=5) == TRI_EINVAL            # pointer count
+    assert _create(L, _desc(), null_at=3) == TRI_EINVAL      # null weight
+    assert _create(L, _desc(), buf=0) == TRI_EINVAL          # null model buffer
+    assert _create(L, _desc(), nbytes=small - 1) == TRI_ECAPACITY
+    assert _create(L, _desc(), buf=0x100010) == TRI_EINVAL   # misaligned buffer
+    assert b"aligned" in L.tri_last_error()
 
 
 def test_kernel_entry_points_validate_on_host(L):

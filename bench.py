@@ -126,7 +126,8 @@ def main():
                      shape.vocab, tensors, dtype=tm.TRI_BF16)
     del tensors  # the model holds its own packed copy
     torch.cuda.empty_cache()
-    max_ctx = args.prompt + (k + 1) * (args.steps + args.warmup + 2) + 64
+    prof_rounds = max(8, args.steps // 4)
+    max_ctx = args.prompt + (k + 1) * (args.steps + args.warmup + prof_rounds + 2) + 64
     sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=128, device=dev)
     prompt = seeded.prompt(args.prompt, shape.vocab)
     t1 = time.perf_counter()
@@ -139,8 +140,6 @@ def main():
         sess.decode_step(tm.TRI_SELFSPEC, k)
     torch.cuda.synchronize()
     L0 = len(sess.state(0)[0])
-    sess.profile(0)  # gate/up GEMM launches
-    torch.cuda.synchronize()
     t_start = time.perf_counter()
     committed, accepts = 0, []
     for _ in range(args.steps):
@@ -149,8 +148,6 @@ def main():
         accepts.append(st[0][2])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    gu_ms, gu_n = sess.profile_read()
-    sess.profile(-1)
     L1 = len(sess.state(0)[0])
     assert L1 - L0 == committed
     ms_per_step = elapsed * 1e3 / args.steps
@@ -159,6 +156,16 @@ def main():
     tpr = committed / args.steps
     value = committed / elapsed
     log(f"{args.steps} rounds in {elapsed:.3f}s: {value:.1f} tok/s, TPR {tpr:.2f}, {ms_per_step:.2f} ms/round")
+
+    # roofline of the dominant kernel: HIP events on the session stream around
+    # every gate/up GEMM launch of further rounds (outside the timed region: the
+    # event records themselves add a few microseconds per launch)
+    sess.profile(0)
+    for _ in range(prof_rounds):
+        sess.decode_step(tm.TRI_SELFSPEC, k)
+    torch.cuda.synchronize()
+    gu_ms, gu_n = sess.profile_read()
+    sess.profile(-1)
 
     # whole-forward HBM fraction: algorithmic bytes of the two forwards of a round
     rows_draft = k + 1

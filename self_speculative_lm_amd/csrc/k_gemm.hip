@@ -37,14 +37,12 @@ constexpr int MAX_S = 16;        // split-K slots (a LoRA slot may be added by t
 constexpr int WAVES_PER_WG = 8;  // waves per gemm workgroup, 16 features each
 constexpr int GROUP = 16 * WAVES_PER_WG;  // rows per packing group (one workgroup's features)
 
-// K is padded with zero weights to a whole number of stages in the packed
-// layout, so every stage of every split is full.
 __host__ __device__ __forceinline__ int kpad(int K) { return (K + KC - 1) / KC * KC; }
 
 struct GemmArgs {
   const bf16_t* X;
-  int M, K, Kp;  // Kp = kpad(K)
-  const bf16_t* W;  // packed
+  int M, K;
+  const bf16_t* W;  // packed (step-major, see pack_bf16_kernel)
   int N, Ks, S;
   int nfb, ntiles;  // feature blocks; tiles = (M tiles) x nfb x S
   float* P;
@@ -55,26 +53,25 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Packed element offset of fragment (row tile i, k-step s) for kpad(K)/32 = ks32 k-steps.
-__host__ __device__ __forceinline__ size_t frag_offset(int i, int s, int ks32) {
-  return ((((size_t)(i >> 3) * ks32 + s) << 3) + (i & 7)) * 512;
-}
-
-// Repack W (up to three row segments, row-major [rows][K]) into fragment
-// order; rows past N and columns past K are zero.  One thread per 16-byte piece.
+// Step-major packed layout of W for a plan (S splits of Ks, nfb blocks of 128
+// features, G = nfb*S workgroup slots g = y*nfb + x).  A block is the 8 KiB one
+// workgroup reads at one k-step: 8 fragments of 16 features x 32 k in MFMA A
+// order (lane l holds feature 16w + l%16, k 8(l/16) .. +8).  Block (j, g), the
+// j-th k-step of split y for feature block x, sits at index j*G + g, so at
+// every k-step the workgroups of a launch read one contiguous window: measured
+// on MI355X this sustains the linear-read rate, whereas one contiguous region
+// per workgroup fell about 10% short.  K is zero-padded to S*Ks.
 __global__ void pack_bf16_kernel(const bf16_t* w0, const bf16_t* w1, const bf16_t* w2, int r0, int r1, int N,
-                                 int K, size_t npieces, bf16_t* dst) {
-  const int ks32 = kpad(K) / 32;
+                                 int K, int nfb, int S, int steps, size_t npieces, bf16_t* dst) {
+  const int G = nfb * S;
   for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < npieces;
        p += (size_t)gridDim.x * blockDim.x) {
-    const size_t f = p >> 6;
-    const int lane = (int)(p & 63);
-    const int i_in = (int)(f & 7);
-    const size_t gs = f >> 3;
-    const int s = (int)(gs % ks32);
-    const int grp = (int)(gs / ks32);
-    const int row = (grp * 8 + i_in) * 16 + (lane & 15);
-    const int k = s * 32 + (lane >> 4) * 8;
+    const size_t blk = p >> 9;
+    const int w = (int)((p >> 6) & 7), lane = (int)(p & 63);
+    const int j = (int)(blk / G), g = (int)(blk % G);
+    const int x = g % nfb, y = g / nfb;
+    const int row = (x * 8 + w) * 16 + (lane & 15);
+    const int k = (y * steps + j) * 32 + (lane >> 4) * 8;
     bf16x8 v = {};
     if (row < N && k < K) {
       const bf16_t* src;
@@ -103,48 +100,51 @@ __global__ void pack_f32_kernel(const float* w0, const float* w1, const float* w
   }
 }
 
-// One workgroup per tile t = (M tile z, K split y, feature block x), x
-// fastest.  Wave w of a workgroup owns row tile i = x*WAVES + w (features
-// [16i, 16i+16)) and writes it to the split's partial slot.
+// One workgroup per tile (M tile z, K split y, feature block x), x fastest:
+// blockIdx.x = z*G + g with g = y*nfb + x.  Wave w owns features
+// [128x + 16w, +16) and writes them to split y's partial slot.
 //
-// A split is processed in passes of NCH stages of KC = 256 k.  Every pass is
-// straight-line code (NCH is a template argument and the stage loop is fully
-// unrolled): the W fragments of stage c+1 are in flight while stage c
-// multiplies, X is double-buffered in LDS, and each stage issues its X loads
-// before its W loads so that staging X waits for those loads only.  Every
-// stage is full (K is padded with zero weights) and rows past M read a
-// clamped row whose results are never stored, so no load is conditional.
+// A split is processed in passes of NCH stages of KC = 256 k (8 k-steps).
+// Every pass is straight-line code (NCH is a template argument and the loops
+// are fully unrolled).  Each wave keeps a ring of D W fragments in flight: the
+// load for k-step j + D is issued right after the MFMAs of k-step j, and a
+// scheduling barrier keeps the compiler from hoisting the loads (few loads in
+// flight per wave, all workgroups reading one window, measured fastest).  X
+// is double-buffered per stage in LDS; each stage's X loads are issued before
+// the stage's W loads.  Rows past M read a clamped row whose results are never
+// stored and padded k has zero weights, so no load is conditional.
 //
 // No W fragment is carried across a loop back-edge: with a runtime stage loop
 // (fragments kept in registers from one iteration to the next) this compiler
 // reused the upper half of a live 16x16x32 MFMA operand for other values, a
 // miscompile that the operand check over the built assembly detects.
-template <int MT, int NCH>
+template <int MT, int NCH, int D>
 __global__ __launch_bounds__(WAVES_PER_WG * 64) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int WAVES = WAVES_PER_WG, NT = WAVES * 64;
+  constexpr int WAVES = WAVES_PER_WG, NT = WAVES * 64, NS = NCH * KSTEPS;
   constexpr int XPIECES = MT * 16 * (KC / 8);  // 16-byte pieces of one X stage
   constexpr int XPT = XPIECES / NT;             // pieces per thread
   static_assert(XPIECES % NT == 0, "every thread stages the same number of X pieces");
+  static_assert(D >= 1 && D <= KSTEPS, "ring depth");
   __shared__ bf16x8 xs[2][KSTEPS][MT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int fbx = blockIdx.x % a.nfb;
-  const int rest = blockIdx.x / a.nfb;
-  const int y = rest % a.S;
-  const int m0 = (rest / a.S) * (MT * 16);
-  const int tile = fbx * WAVES + wave;
+  const int G = a.nfb * a.S;
+  const int g = blockIdx.x % G;
+  const int m0 = (blockIdx.x / G) * (MT * 16);
+  const int fbx = g % a.nfb, y = g / a.nfb;
   const int kbeg = y * a.Ks;
-  const int npass = (min(a.Kp, kbeg + a.Ks) - kbeg) / (NCH * KC);
-  const bf16_t* wt0 = a.W + frag_offset(tile, kbeg >> 5, a.Kp / 32) + lane * 8;
+  const int npass = a.Ks / (NCH * KC);
+  const size_t wstep = (size_t)G * (WAVES * 512);  // elements between k-steps
+  const bf16_t* wb = a.W + (size_t)g * (WAVES * 512) + wave * 512 + lane * 8;
 
-  // B operand staging: xs[b][s][t][g*16 + j] = X[m0 + 16t + j][k + 32s + 8g .. +8]
+  // B operand staging: xs[b][s][t][gg*16 + j] = X[m0 + 16t + j][k + 32s + 8gg .. +8]
   const bf16_t* xrow[XPT];
   int xk[XPT];
 #pragma unroll
   for (int it = 0; it < XPT; ++it) {
     const int i = tid + it * NT;
-    const int g = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
+    const int gg = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
     xrow[it] = a.X + (size_t)min(m0 + r, a.M - 1) * a.K;
-    xk[it] = s * 32 + g * 8;
+    xk[it] = s * 32 + gg * 8;
   }
   f32x4 acc[MT];
 #pragma unroll
@@ -152,41 +152,39 @@ __global__ __launch_bounds__(WAVES_PER_WG * 64) void gemm_bf16_kernel(GemmArgs a
 
   for (int p = 0; p < npass; ++p) {
     const int k0 = kbeg + p * (NCH * KC);
-    const bf16_t* wt = wt0 + (size_t)p * NCH * (KSTEPS * 8 * 512);
-    bf16x8 w[2][KSTEPS], xr[XPT];
+    const bf16_t* wp = wb + (size_t)p * NS * wstep;
+    bf16x8 ring[D], xr[XPT];
     auto load_x = [&](int c) {
 #pragma unroll
       for (int it = 0; it < XPT; ++it)
-        xr[it] = ld16(xrow[it] + min(k0 + c * KC + xk[it], a.K - 8));  // padded K: zero weights there
-    };
-    auto load_w = [&](int c, bf16x8* wf) {
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) wf[s] = ld16(wt + (size_t)(c * KSTEPS + s) * (8 * 512));
+        xr[it] = ld16(xrow[it] + min(k0 + c * KC + xk[it], a.K - 8));  // padded k: zero weights there
     };
     auto store_x = [&](int b) {
 #pragma unroll
       for (int it = 0; it < XPT; ++it) {
         const int i = tid + it * NT;
-        const int g = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
-        xs[b][s][r >> 4][g * 16 + (r & 15)] = xr[it];
+        const int gg = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
+        xs[b][s][r >> 4][gg * 16 + (r & 15)] = xr[it];
       }
     };
     if (p > 0) __syncthreads();  // the previous pass's last stage still reads xs
     load_x(0);
-    load_w(0, w[0]);
+#pragma unroll
+    for (int i = 0; i < D; ++i) ring[i] = ld16(wp + (size_t)i * wstep);
     store_x(0);
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      if (c + 1 < NCH) {
-        load_x(c + 1);
-        load_w(c + 1, w[(c + 1) & 1]);
-      }
+      if (c + 1 < NCH) load_x(c + 1);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
+      for (int s = 0; s < KSTEPS; ++s) {
+        const int j = c * KSTEPS + s;
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[c & 1][s], xs[c & 1][s][t][lane], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[j % D], xs[c & 1][s][t][lane], acc[t], 0, 0, 0);
+        if (j + D < NS) ring[j % D] = ld16(wp + (size_t)(j + D) * wstep);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (c + 1 < NCH) {
         store_x((c + 1) & 1);
         __syncthreads();
@@ -195,7 +193,7 @@ __global__ __launch_bounds__(WAVES_PER_WG * 64) void gemm_bf16_kernel(GemmArgs a
   }
   // D layout: lane l holds D[4*(l/16) + r][l%16] = Y[m0 + 16t + l%16][n0 + 4*(l/16) + r]
   float* out = a.P + (size_t)y * a.slot_stride;
-  const int nn = tile * 16 + 4 * (lane >> 4);
+  const int nn = (fbx * WAVES + wave) * 16 + 4 * (lane >> 4);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = m0 + t * 16 + (lane & 15);
@@ -223,23 +221,26 @@ __global__ __launch_bounds__(64) void gemm_f32_kernel(const float* X, int M, int
 }
 
 template <int MT, int NCH>
-void launch_tiles(const GemmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<MT, NCH>), dim3(a.ntiles), dim3(WAVES_PER_WG * 64), 0, st, a);
+void launch_tiles(const GemmArgs& a, int depth, hipStream_t st) {
+  if (depth == 2)
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, NCH, 2>), dim3(a.ntiles), dim3(WAVES_PER_WG * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<MT, NCH, 4>), dim3(a.ntiles), dim3(WAVES_PER_WG * 64), 0, st, a);
 }
 
 template <int MT>
 hipError_t launch_mt(GemmArgs a, const GemmPlan& p, int M, hipStream_t st) {
-  a.nfb = (a.N + 16 * WAVES_PER_WG - 1) / (16 * WAVES_PER_WG);
+  a.nfb = (a.N + GROUP - 1) / GROUP;
   a.S = p.S;
   a.ntiles = a.nfb * p.S * ((M + 16 * MT - 1) / (16 * MT));
   switch (p.nch) {
-    case 1: launch_tiles<MT, 1>(a, st); break;
-    case 2: launch_tiles<MT, 2>(a, st); break;
-    case 3: launch_tiles<MT, 3>(a, st); break;
-    case 4: launch_tiles<MT, 4>(a, st); break;
-    case 5: launch_tiles<MT, 5>(a, st); break;
-    case 6: launch_tiles<MT, 6>(a, st); break;
-    case 8: launch_tiles<MT, 8>(a, st); break;
+    case 1: launch_tiles<MT, 1>(a, p.depth, st); break;
+    case 2: launch_tiles<MT, 2>(a, p.depth, st); break;
+    case 3: launch_tiles<MT, 3>(a, p.depth, st); break;
+    case 4: launch_tiles<MT, 4>(a, p.depth, st); break;
+    case 5: launch_tiles<MT, 5>(a, p.depth, st); break;
+    case 6: launch_tiles<MT, 6>(a, p.depth, st); break;
+    case 8: launch_tiles<MT, 8>(a, p.depth, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
@@ -273,7 +274,8 @@ GemmPlan gemm_plan(int N, int K, int dtype, bool unsplit) {
     tgt = 512 / KC;
   tgt = std::max(1, std::min(tgt, T));
   // Prefer a split count that divides the stages evenly, within a factor of
-  // two of the target; otherwise the last split is shorter.
+  // two of the target; otherwise every split is padded to the same length
+  // with zero weights (the packed layout needs equal splits).
   const int S0 = std::min((T + tgt - 1) / tgt, MAX_S);
   int S = 0;
   for (int d = 0; d <= S0 && !S; ++d)
@@ -283,38 +285,35 @@ GemmPlan gemm_plan(int N, int K, int dtype, bool unsplit) {
   const int ps = (T + S - 1) / S;  // stages per split
   p.S = (T + ps - 1) / ps;
   p.Ks = ps * KC;
-  const int last = T - (p.S - 1) * ps;
-  int g = ps;  // gcd(ps, last): a pass length that divides both split lengths
-  for (int b = last; b;) {
-    const int t = g % b;
-    g = b;
-    b = t;
-  }
   p.nch = 1;
   for (int c : {8, 6, 5, 4, 3, 2})
-    if (g % c == 0) {
+    if (ps % c == 0) {
       p.nch = c;
       break;
     }
+  // W fragments in flight per wave: 2 k-steps for the wide gate/up shape,
+  // 4 elsewhere (measured).
+  p.depth = (!unsplit && N >= 16384) ? 2 : 4;
   return p;
 }
 
-size_t gemm_packed_bytes(int N, int K, int dtype) {
-  if (dtype == TRI_BF16) return (size_t)((N + GROUP - 1) / GROUP) * GROUP * kpad(K) * 2;
+size_t gemm_packed_bytes(const GemmPlan& p, int N, int K, int dtype) {
+  if (dtype == TRI_BF16) return (size_t)((N + GROUP - 1) / GROUP) * GROUP * ((size_t)p.S * p.Ks) * 2;
   return (size_t)N * K * 4;
 }
 
-hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, void* dst, hipStream_t st) {
+hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, const GemmPlan& p, void* dst,
+                       hipStream_t st) {
   const void* w0 = segs[0].ptr;
   const void* w1 = nseg > 1 ? segs[1].ptr : nullptr;
   const void* w2 = nseg > 2 ? segs[2].ptr : nullptr;
   const int r0 = segs[0].rows;
   const int r1 = nseg > 1 ? segs[1].rows : 0;
   if (dtype == TRI_BF16) {
-    const size_t npieces = gemm_packed_bytes(N, K, dtype) / 16;
+    const size_t npieces = gemm_packed_bytes(p, N, K, dtype) / 16;
     hipLaunchKernelGGL(pack_bf16_kernel, dim3(2048), dim3(256), 0, st, static_cast<const bf16_t*>(w0),
-                       static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w2), r0, r1, N, K, npieces,
-                       static_cast<bf16_t*>(dst));
+                       static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w2), r0, r1, N, K,
+                       (N + GROUP - 1) / GROUP, p.S, p.Ks / 32, npieces, static_cast<bf16_t*>(dst));
   } else {
     hipLaunchKernelGGL(pack_f32_kernel, dim3(2048), dim3(256), 0, st, static_cast<const float*>(w0),
                        static_cast<const float*>(w1), static_cast<const float*>(w2), r0, r1, N, K,
@@ -331,7 +330,6 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
     a.X = static_cast<const bf16_t*>(X);
     a.M = M;
     a.K = K;
-    a.Kp = kpad(K);
     a.W = static_cast<const bf16_t*>(W);
     a.N = N;
     a.Ks = plan.Ks;

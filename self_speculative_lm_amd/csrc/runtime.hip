@@ -681,8 +681,27 @@ struct ModelLayout {
   std::vector<L> layers;
 };
 
+// GEMM plans of a model; the packed weight layout depends on them.
+struct ModelPlans {
+  GemmPlan qkv, o, gu, down, lm, la, lb;
+};
+
+ModelPlans model_plans(const tri_model_desc& d) {
+  const int qd = d.n_q_heads * d.head_dim, kd = d.n_kv_heads * d.head_dim;
+  ModelPlans P;
+  P.qkv = gemm_plan(qd + 2 * kd, d.d_model, d.dtype);
+  P.o = gemm_plan(d.d_model, qd, d.dtype);
+  P.gu = gemm_plan(2 * d.d_ffn, d.d_model, d.dtype);
+  P.down = gemm_plan(d.d_model, d.d_ffn, d.dtype);
+  P.lm = gemm_plan(d.vocab, d.d_model, d.dtype, /*unsplit=*/true);
+  P.la = d.lora_rank > 0 ? gemm_plan(d.lora_rank, qd, d.dtype) : GemmPlan{1, qd};
+  P.lb = d.lora_rank > 0 ? gemm_plan(d.d_model, d.lora_rank, d.dtype) : GemmPlan{0, 0};
+  return P;
+}
+
 ModelLayout model_layout(const tri_model_desc& d) {
   ModelLayout M;
+  const ModelPlans P = model_plans(d);
   const size_t esz = d.dtype == TRI_BF16 ? 2 : 4;
   const int qd = d.n_q_heads * d.head_dim, kd = d.n_kv_heads * d.head_dim;
   size_t off = 0;
@@ -694,17 +713,17 @@ ModelLayout model_layout(const tri_model_desc& d) {
   M.embed = take((size_t)(d.vocab + 1) * d.d_model * esz);
   M.layers.resize(d.n_layers);
   for (auto& L : M.layers) {
-    L.qkv = take(gemm_packed_bytes(qd + 2 * kd, d.d_model, d.dtype));
-    L.o = take(gemm_packed_bytes(d.d_model, qd, d.dtype));
-    L.gu = take(gemm_packed_bytes(2 * d.d_ffn, d.d_model, d.dtype));
-    L.down = take(gemm_packed_bytes(d.d_model, d.d_ffn, d.dtype));
+    L.qkv = take(gemm_packed_bytes(P.qkv, qd + 2 * kd, d.d_model, d.dtype));
+    L.o = take(gemm_packed_bytes(P.o, d.d_model, qd, d.dtype));
+    L.gu = take(gemm_packed_bytes(P.gu, 2 * d.d_ffn, d.d_model, d.dtype));
+    L.down = take(gemm_packed_bytes(P.down, d.d_model, d.d_ffn, d.dtype));
     L.n1 = take((size_t)d.d_model * 4);
     L.n2 = take((size_t)d.d_model * 4);
-    L.la = d.lora_rank > 0 ? take(gemm_packed_bytes(d.lora_rank, qd, d.dtype)) : 0;
-    L.lb = d.lora_rank > 0 ? take(gemm_packed_bytes(d.d_model, d.lora_rank, d.dtype)) : 0;
+    L.la = d.lora_rank > 0 ? take(gemm_packed_bytes(P.la, d.lora_rank, qd, d.dtype)) : 0;
+    L.lb = d.lora_rank > 0 ? take(gemm_packed_bytes(P.lb, d.d_model, d.lora_rank, d.dtype)) : 0;
   }
   M.final_norm = take((size_t)d.d_model * 4);
-  M.lm_head = take(gemm_packed_bytes(d.vocab, d.d_model, d.dtype));
+  M.lm_head = take(gemm_packed_bytes(P.lm, d.vocab, d.d_model, d.dtype));
   M.total = off;
   return M;
 }
@@ -732,6 +751,7 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   for (int i = 0; i < n_weights; ++i)
     if (!weights[i]) return fail(TRI_EINVAL, "weight pointer %d is null", i);
   const ModelLayout ML = model_layout(d);
+  const ModelPlans P = model_plans(d);
   if (bytes < ML.total) return fail(TRI_ECAPACITY, "model buffer has %zu bytes, needs %zu", bytes, ML.total);
   if (reinterpret_cast<uintptr_t>(model_buf) & 255) return fail(TRI_EINVAL, "model buffer must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -747,13 +767,13 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   for (int l = 0; l < d.n_layers; ++l) {
     const ModelLayout::L& L = ML.layers[l];
     WSeg qkv[3] = {{weights[w], qd}, {weights[w + 1], kd}, {weights[w + 2], kd}};
-    HIPCHK(launch_pack(dt, qkv, 3, qd + 2 * kd, d.d_model, base + L.qkv, st));
+    HIPCHK(launch_pack(dt, qkv, 3, qd + 2 * kd, d.d_model, P.qkv, base + L.qkv, st));
     WSeg o = {weights[w + 3], d.d_model};
-    HIPCHK(launch_pack(dt, &o, 1, d.d_model, qd, base + L.o, st));
+    HIPCHK(launch_pack(dt, &o, 1, d.d_model, qd, P.o, base + L.o, st));
     WSeg gu[2] = {{weights[w + 4], d.d_ffn}, {weights[w + 5], d.d_ffn}};
-    HIPCHK(launch_pack(dt, gu, 2, 2 * d.d_ffn, d.d_model, base + L.gu, st));
+    HIPCHK(launch_pack(dt, gu, 2, 2 * d.d_ffn, d.d_model, P.gu, base + L.gu, st));
     WSeg dn = {weights[w + 6], d.d_model};
-    HIPCHK(launch_pack(dt, &dn, 1, d.d_model, d.d_ffn, base + L.down, st));
+    HIPCHK(launch_pack(dt, &dn, 1, d.d_model, d.d_ffn, P.down, base + L.down, st));
     HIPCHK(hipMemcpyAsync(base + L.n1, weights[w + 7], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(hipMemcpyAsync(base + L.n2, weights[w + 8], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
     w += 9;
@@ -761,14 +781,14 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   HIPCHK(hipMemcpyAsync(base + ML.final_norm, weights[w++], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
   {
     WSeg lm = {weights[w++], d.vocab};
-    HIPCHK(launch_pack(dt, &lm, 1, d.vocab, d.d_model, base + ML.lm_head, st));
+    HIPCHK(launch_pack(dt, &lm, 1, d.vocab, d.d_model, P.lm, base + ML.lm_head, st));
   }
   if (d.lora_rank > 0)
     for (int l = 0; l < d.n_layers; ++l) {
       WSeg a = {weights[w++], d.lora_rank};
-      HIPCHK(launch_pack(dt, &a, 1, d.lora_rank, qd, base + ML.layers[l].la, st));
+      HIPCHK(launch_pack(dt, &a, 1, d.lora_rank, qd, P.la, base + ML.layers[l].la, st));
       WSeg b = {weights[w++], d.d_model};
-      HIPCHK(launch_pack(dt, &b, 1, d.d_model, d.lora_rank, base + ML.layers[l].lb, st));
+      HIPCHK(launch_pack(dt, &b, 1, d.d_model, d.lora_rank, P.lb, base + ML.layers[l].lb, st));
     }
   HIPCHK(hipStreamSynchronize(st));
   tri_model* m = new tri_model();
@@ -791,13 +811,13 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   m->final_norm = reinterpret_cast<const float*>(base + ML.final_norm);
   m->lm_head = base + ML.lm_head;
   m->qkv_n = qd + 2 * kd;
-  m->p_qkv = gemm_plan(m->qkv_n, d.d_model, d.dtype);
-  m->p_o = gemm_plan(d.d_model, qd, d.dtype);
-  m->p_gu = gemm_plan(2 * d.d_ffn, d.d_model, d.dtype);
-  m->p_down = gemm_plan(d.d_model, d.d_ffn, d.dtype);
-  m->p_lm = gemm_plan(d.vocab, d.d_model, d.dtype, /*unsplit=*/true);
-  m->p_la = d.lora_rank > 0 ? gemm_plan(d.lora_rank, qd, d.dtype) : GemmPlan{1, qd};
-  m->p_lb = d.lora_rank > 0 ? gemm_plan(d.d_model, d.lora_rank, d.dtype) : GemmPlan{0, 0};
+  m->p_qkv = P.qkv;
+  m->p_o = P.o;
+  m->p_gu = P.gu;
+  m->p_down = P.down;
+  m->p_lm = P.lm;
+  m->p_la = P.la;
+  m->p_lb = P.lb;
   *out = m;
   return TRI_OK;
 }

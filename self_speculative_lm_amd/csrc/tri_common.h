@@ -47,16 +47,19 @@ struct WSeg {
   int rows;
 };
 struct GemmPlan {
-  int S;        // K splits (partial slots)
-  int Ks;       // K per split (bf16: a multiple of the 256-wide stage)
-  int nch = 1;  // bf16: stages per straight-line pass (divides every split's stages)
+  int S;          // K splits (partial slots)
+  int Ks;         // K per split (bf16: a multiple of the 256-wide stage; K padded to S*Ks)
+  int nch = 1;    // bf16: stages per straight-line pass (divides Ks / 256)
+  int depth = 4;  // bf16: W fragments in flight per wave
 };
 // unsplit: one K split whatever the shape (the lm_head writes logits directly).
 GemmPlan gemm_plan(int N, int K, int dtype, bool unsplit = false);
-// Bytes of a packed weight matrix (bf16: MFMA-fragment order, rows padded to
-// 128; float32: row-major) and the packing launch (segments concatenated).
-size_t gemm_packed_bytes(int N, int K, int dtype);
-hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, void* dst, hipStream_t st);
+// Bytes of a packed weight matrix for a plan (bf16: step-major MFMA fragments,
+// rows padded to 128, K padded to S*Ks; float32: row-major) and the packing
+// launch (segments concatenated by rows).
+size_t gemm_packed_bytes(const GemmPlan& p, int N, int K, int dtype);
+hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, const GemmPlan& p, void* dst,
+                       hipStream_t st);
 // Y = X W^T with W packed by launch_pack.
 hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, int N, const GemmPlan& plan,
                        float* P, size_t slot_stride, hipStream_t st);

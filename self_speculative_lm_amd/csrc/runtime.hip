@@ -912,6 +912,9 @@ int tri_session_create(const tri_model* m, int max_batch, int max_ctx, int max_r
     }
   e = hipMemcpyAsync(s->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, s->st);
   if (e == hipSuccess) e = hipMemcpyAsync(s->dints, s->hints, S.nints * 4, hipMemcpyHostToDevice, s->st);
+  // The KV cache starts cleared: attention stages whole 64-key tiles, so slots
+  // past a sequence's length are read (and masked) and must hold finite values.
+  if (e == hipSuccess) e = launch_zero_f32(reinterpret_cast<float*>(s->kbuf), (S.v - S.k) / 4 * 2, s->st);
   if (e == hipSuccess) e = hipStreamSynchronize(s->st);
   if (e != hipSuccess) {
     for (hipEvent_t ev : s->meta_ev) (void)hipEventDestroy(ev);

@@ -78,7 +78,7 @@ struct AttnLaunch {
   void* out;
   float* part;  // split partials
 };
-int attn_pick_split(int max_hi);
+int attn_pick_split(int max_ctx);
 size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split);
 hipError_t launch_attn(int dtype, const AttnLaunch& a, hipStream_t st);
 

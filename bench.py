@@ -51,10 +51,28 @@ def gu_bytes_per_launch(shape, rows):
     return 2 * f * d * 2 + rows * d * 2 + rows * 2 * f * 4
 
 
-def cpu_baseline(shape, prefix, k, tpr):
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed PMC summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what the counter reads for a plain copy of known
+    size), or None when the GEMM source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_gateup_8b_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(shape, prefix, k, tpr, repeats=5):
     """The oracle on the host cores: one draft forward (1 + k rows) and one
     verify forward (k rows) over 1- and 2-layer slices of the model with a
-    prefix-long cache, extrapolated to all layers (per-layer time = t2 - t1)."""
+    prefix-long cache, each timed `repeats` times (about 10 s of CPU work in
+    all); the mean times are extrapolated to all layers (per-layer time =
+    t2 - t1)."""
     import dataclasses
 
     import numpy as np
@@ -66,30 +84,36 @@ def cpu_baseline(shape, prefix, k, tpr):
     except Exception:
         threads = os.cpu_count() or 1
     times = {}
+    total = 0.0
     for nl in (1, 2):
         sl = dataclasses.replace(shape, name=f"{shape.name}-slice{nl}", n_layers=nl)
         om = OracleModel(sl, seeded.gen_weights(sl), batched_linear=True, keep_float32=True)
-        cache = KVCache(sl, prefix + k + 1)
         rng = np.random.default_rng(0)
-        for arr in (cache.k, cache.v):
-            arr[:, :prefix] = rng.standard_normal(arr[:, :prefix].shape).astype(np.float32)
         L = prefix + 1
         draft = [Row(1, L - 1, L)] + [Row(shape.vocab, L + i, L + k, False) for i in range(k)]
         verify = [Row(2 + i, L + i, L + i + 1) for i in range(k)]
-        t0 = time.perf_counter()
-        forward(om, cache, draft)
-        forward(om, cache, verify)
-        times[nl] = time.perf_counter() - t0
+        ts = []
+        for _ in range(repeats):
+            cache = KVCache(sl, prefix + k + 1)
+            for arr in (cache.k, cache.v):
+                arr[:, :prefix] = rng.standard_normal(arr[:, :prefix].shape).astype(np.float32)
+            t0 = time.perf_counter()
+            forward(om, cache, draft)
+            forward(om, cache, verify)
+            ts.append(time.perf_counter() - t0)
+        times[nl] = sum(ts) / len(ts)
+        total += sum(ts)
         del om, cache
     per_layer = times[2] - times[1]
     head = times[1] - per_layer
     round_s = head + shape.n_layers * per_layer
     return {"value": round(tpr / round_s, 4), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"float64 oracle, one draft ({k + 1} rows) + one verify ({k} rows) forward over 1- and "
-                       f"2-layer slices of the 8B-class model with a {prefix}-token cache; per-layer time "
-                       f"{per_layer:.2f}s, lm_head+sampling {head:.2f}s, extrapolated to {shape.n_layers} layers "
-                       f"= {round_s:.1f}s per round at the GPU's measured {tpr:.2f} tokens/round"),
-            "seconds_measured": round(times[1] + times[2], 2)}
+            "sample": (f"float64 oracle (float32-stored weights, batched row products), one draft ({k + 1} rows) + "
+                       f"one verify ({k} rows) forward over 1- and 2-layer slices of the 8B-class model with a "
+                       f"{prefix}-token cache, {repeats} times each; mean per-layer time {per_layer:.3f}s, "
+                       f"lm_head+sampling {head:.2f}s, extrapolated to {shape.n_layers} layers = {round_s:.1f}s per "
+                       f"round at the GPU's measured {tpr:.2f} tokens/round"),
+            "seconds_measured": round(total, 2)}
 
 
 def main():
@@ -101,6 +125,8 @@ def main():
     ap.add_argument("--block", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-replay", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the decode step is built and measured on a single "
@@ -130,6 +156,13 @@ def main():
     max_ctx = args.prompt + (k + 1) * (args.steps + args.warmup + prof_rounds + 2) + 64
     sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=128, device=dev)
     prompt = seeded.prompt(args.prompt, shape.vocab)
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)  # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     t1 = time.perf_counter()
     sess.prefill(0, prompt)
     torch.cuda.synchronize()
@@ -192,7 +225,8 @@ def main():
         "round_algorithmic_GBps": round(round_gbs, 1),
         "prefill_ms": round(prefill_s * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (PMC FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)",
                      "kernel": "gemm_bf16_kernel (gate/up projection, N=24576, K=4096)",
                      "avg_launch_us": round(gu_avg_ms * 1e3, 2), "launches": gu_n,
                      "algorithmic_bytes_per_launch": int(gu_bytes)},

@@ -44,13 +44,20 @@ class Row:
 
 class OracleModel:
     """Weights in float64 plus the shape; ``batched_linear`` trades exact
-    row independence of the projections for speed on large models."""
+    row independence of the projections for speed on large models.
+
+    ``proj_dtype=np.float32`` evaluates the projections (the matrix products)
+    in float32 instead of float64, everything else unchanged.  It is not the
+    oracle of any parity claim: it measures how far the float64 result moves
+    when the products are accumulated at float32 precision, the floor any
+    float32-accumulating implementation sits on."""
 
     def __init__(self, shape, weights: Dict[str, np.ndarray], batched_linear: bool = False,
-                 keep_float32: bool = False):
+                 keep_float32: bool = False, proj_dtype=np.float64):
         self.shape = shape
         self.bf16 = shape.dtype == "bf16"
         self.batched_linear = batched_linear
+        self.proj_dtype = np.dtype(proj_dtype)
         conv = (lambda a: np.asarray(a, dtype=np.float32)) if keep_float32 else \
             (lambda a: np.asarray(a, dtype=np.float64))
         self.w = {k: conv(v) for k, v in weights.items()}
@@ -66,17 +73,21 @@ def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
 
 
-def linear(x: np.ndarray, w: np.ndarray, batched: bool) -> np.ndarray:
-    """y = x W^T for each row of x.
+def linear(x: np.ndarray, w: np.ndarray, batched: bool, dtype=np.float64) -> np.ndarray:
+    """y = x W^T for each row of x, computed in ``dtype`` (float64 unless the
+    model asks for the float32 sensitivity reference) and returned in float64.
 
     By default each row is its own matrix-vector product, so a row's result
     never depends on which other rows share the forward (this is what makes
     oracle self-speculation bit-identical to oracle AR).
     """
-    w = np.asarray(w, dtype=np.float64)
+    w = np.asarray(w, dtype=dtype)
+    x = np.asarray(x, dtype=dtype)
     if batched:
-        return x @ w.T
-    return np.stack([w @ xi for xi in x]) if len(x) else np.zeros((0, w.shape[0]))
+        y = x @ w.T
+    else:
+        y = np.stack([w @ xi for xi in x]) if len(x) else np.zeros((0, w.shape[0]), dtype=dtype)
+    return np.asarray(y, dtype=np.float64)
 
 
 def rope_angles(pos: int, head_dim: int, base: float) -> np.ndarray:
@@ -152,14 +163,15 @@ def forward(model: OracleModel, cache: KVCache, rows: List[Row],
     hq, hkv, hd = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
     group = hq // hkv
     bl = model.batched_linear
+    pd = model.proj_dtype
     x = np.stack([np.asarray(w["embed"][r.token], dtype=np.float64) for r in rows])
     use_lora = lora_enabled and model.has_lora
     for l in range(sh.n_layers):
         p = f"layers.{l}."
         y = st(rms_norm(x, w[p + "attn_norm"], sh.rms_eps))
-        q = linear(y, w[p + "wq"], bl).reshape(n, hq, hd)
-        k = linear(y, w[p + "wk"], bl).reshape(n, hkv, hd)
-        v = linear(y, w[p + "wv"], bl).reshape(n, hkv, hd)
+        q = linear(y, w[p + "wq"], bl, pd).reshape(n, hq, hd)
+        k = linear(y, w[p + "wk"], bl, pd).reshape(n, hkv, hd)
+        v = linear(y, w[p + "wv"], bl, pd).reshape(n, hkv, hd)
         for i, r in enumerate(rows):
             q[i] = apply_rope(q[i], r.pos, sh.rope_base)
             k[i] = apply_rope(k[i], r.pos, sh.rope_base)
@@ -170,18 +182,18 @@ def forward(model: OracleModel, cache: KVCache, rows: List[Row],
         o = np.stack([attend(q[i], cache.k[l], cache.v[l], r.hi, group).reshape(-1)
                       for i, r in enumerate(rows)])
         o = st(o)
-        delta = linear(o, w[p + "wo"], bl)
+        delta = linear(o, w[p + "wo"], bl, pd)
         if use_lora:
             mask = np.array([r.lora for r in rows])
             if mask.any():
-                mid = st(linear(o[mask], w[f"lora.{l}.a"], bl))
-                delta[mask] = delta[mask] + linear(mid, w[f"lora.{l}.b"], bl)
+                mid = st(linear(o[mask], w[f"lora.{l}.a"], bl, pd))
+                delta[mask] = delta[mask] + linear(mid, w[f"lora.{l}.b"], bl, pd)
         x = x + delta
         y = st(rms_norm(x, w[p + "ffn_norm"], sh.rms_eps))
-        h = st(silu(linear(y, w[p + "w_gate"], bl)) * linear(y, w[p + "w_up"], bl))
-        x = x + linear(h, w[p + "w_down"], bl)
+        h = st(silu(linear(y, w[p + "w_gate"], bl, pd)) * linear(y, w[p + "w_up"], bl, pd))
+        x = x + linear(h, w[p + "w_down"], bl, pd)
     yf = st(rms_norm(x, w["final_norm"], sh.rms_eps))
-    logits = linear(yf, w["lm_head"], bl)
+    logits = linear(yf, w["lm_head"], bl, pd)
     if return_hidden:
         return logits, x
     return logits

@@ -18,8 +18,11 @@
 // V fragment from LDS once for its QT query tiles.  The K rows fed to the
 // MFMA are permuted so that a lane ends up holding 8 scores of one query for 8
 // consecutive keys: the softmax row statistics then need only two cross-lane
-// steps, and the same registers, rounded to bf16, are directly the B operand
-// of O^T = V^T P^T (no LDS round trip for P).  Online softmax in float32
+// steps, and the same registers, rounded to fp16, are directly the B operand
+// of O^T = V^T P^T (no LDS round trip for P).  P.V runs in fp16 (V converted
+// from bf16 when staged, exact inside the fp16 range and saturated at
+// +-65504): P in [0, 1] keeps 11 significant bits instead of bf16's 8, which
+// measurably moved the logits of 4096-wide models.  Online softmax in float32
 // (exp2 with the scale folded in).  Splits write unnormalised partials
 // (O, m, l) that a combine kernel merges in split order; a launch with a
 // single split normalises in place.  A row's result depends only on its own
@@ -30,6 +33,8 @@
 
 namespace tri {
 namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int HD = 128;
 constexpr int KT = 64;
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NREG = NT_ALL > 0 ? NT_ALL : 1;
   static_assert(PIECES % NT == 0, "every thread stages the same number of pieces");
   __shared__ __attribute__((aligned(16))) bf16_t ks[2][KT * KPAD];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[2][HD * VPAD];
+  __shared__ __attribute__((aligned(16))) _Float16 vs[2][HD * VPAD];  // V^T tile in fp16
   __shared__ int s_maxhi;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seq = blockIdx.z / a.hkv, kvh = blockIdx.z - seq * a.hkv;
@@ -91,21 +96,25 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
       vr[u] = ld16(vbase + (size_t)(i >> 3) * a.ctx + t0 + (i & 7) * 8);
     }
   };
-  // vlim < 64: keys of the tile at or past vlim may hold anything (a caller's
-  // cache is not cleared); their scores are masked and their V values are
-  // zeroed here, by the thread that stages them, so that 0 * V is never NaN.
+  // V is converted to fp16 here (exact inside the fp16 range, saturated
+  // outside it).  vlim < 64: keys of the tile at or past vlim may hold
+  // anything (a caller's cache is not cleared); their scores are masked and
+  // their V values are zeroed here, by the thread that stages them, so that
+  // 0 * V is never NaN.
   auto store_tile = [&](int b, const bf16x8* kr, const bf16x8* vr, int vlim) {
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
       const int i = tid + u * NT;
       *reinterpret_cast<bf16x8*>(&ks[b][(i >> 4) * KPAD + (i & 15) * 8]) = kr[u];
-      bf16x8 vv = vr[u];
+      f16x8 vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vv[e] = (_Float16)fminf(fmaxf((float)vr[u][e], -65504.f), 65504.f);
       if (vlim < KT) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if ((i & 7) * 8 + e >= vlim) vv[e] = (__bf16)0.0f;
+          if ((i & 7) * 8 + e >= vlim) vv[e] = (_Float16)0.0f;
       }
-      *reinterpret_cast<bf16x8*>(&vs[b][(i >> 3) * VPAD + (i & 7) * 8]) = vv;
+      *reinterpret_cast<f16x8*>(&vs[b][(i >> 3) * VPAD + (i & 7) * 8]) = vv;
     }
   };
 
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
         }
       }
     }
-    bf16x8 pb[QT][2];
+    f16x8 pb[QT][2];
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
       float tm = tmax[q];
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
         for (int e = 0; e < 8; ++e) {
           const float pv = exp2f(p[q][m][e] - m_new);
           psum += pv;
-          pb[q][m][e] = (__bf16)pv;
+          pb[q][m][e] = (_Float16)pv;
         }
       }
       l_run[q] = l_run[q] * alpha + psum;
@@ -220,10 +229,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
     for (int dt = 0; dt < 8; ++dt) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vs[b][(16 * dt + j) * VPAD + 32 * m + 8 * g]);
+        const f16x8 vf = *reinterpret_cast<const f16x8*>(&vs[b][(16 * dt + j) * VPAD + 32 * m + 8 * g]);
 #pragma unroll
         for (int q = 0; q < QT; ++q)
-          oacc[q][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[q][m], oacc[q][dt], 0, 0, 0);
+          oacc[q][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[q][m], oacc[q][dt], 0, 0, 0);
       }
     }
   };

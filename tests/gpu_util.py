@@ -2,7 +2,7 @@
 GPU forward trace through the oracle (teacher forcing)."""
 from __future__ import annotations
 
-from typing import Dict, List
+from typing import Dict, List, Optional
 
 import numpy as np
 
@@ -28,11 +28,18 @@ def make_model(shape: seeded.ModelShape, tensors):
                     rope_base=shape.rope_base, rms_eps=shape.rms_eps, lora_rank=shape.lora_rank)
 
 
-def replay(shape: seeded.ModelShape, oracle_model: OracleModel, trace: List[dict], max_ctx: int):
+def replay(shape: seeded.ModelShape, oracle_model: OracleModel, trace: List[dict], max_ctx: int,
+           prompts: Optional[List[List[int]]] = None):
     """Run every traced forward through the oracle with the GPU's rows (its
     tokens, positions, limits and LoRA flags): returns per forward the oracle
-    logits (or None when the GPU forward had no lm_head)."""
+    logits (or None when the GPU forward had no lm_head).  With `prompts`, the
+    oracle cache of sequence i first holds the causal prefill of prompts[i]
+    (all but its last token, in one forward), as a GPU prefill leaves it."""
     caches: Dict[int, KVCache] = {}
+    for i, p in enumerate(prompts or []):
+        cache = caches.setdefault(i, KVCache(shape, max_ctx))
+        if len(p) > 1:
+            forward(oracle_model, cache, [Row(int(t), q, q + 1) for q, t in enumerate(p[:-1])])
     out = []
     for rec in trace:
         seqs = rec["seq"]

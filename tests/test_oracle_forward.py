@@ -105,3 +105,20 @@ def test_rms_norm_matches_torch():
     g = rng.standard_normal(96)
     ref = F.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), eps=1e-6).numpy()
     np.testing.assert_allclose(rms_norm(x, g, 1e-6), ref, rtol=1e-13)
+
+
+def test_float32_projection_reference_is_the_same_function():
+    """The float32-projection mode (used only to measure the float32
+    accumulation floor of large shapes) computes the same forward: on the tiny
+    model it agrees with the float64 oracle to float32 rounding, and it does
+    evaluate the products in float32 (the results are not bit-identical)."""
+    import numpy as np
+    import seeded
+    from oracle.model import KVCache, OracleModel, Row, forward
+    shape = seeded.TINY
+    w = seeded.gen_weights(shape)
+    rows = [Row(int(t), p, p + 1) for p, t in enumerate(seeded.prompt(12, shape.vocab))]
+    a = forward(OracleModel(shape, w), KVCache(shape, 16), rows)
+    b = forward(OracleModel(shape, w, proj_dtype=np.float32), KVCache(shape, 16), rows)
+    err = float(np.abs(a - b).max())
+    assert 0.0 < err < 1e-5 * max(1.0, float(np.abs(a).max()))

@@ -16,10 +16,15 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed float32 VALU forms are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source additions.  The attention kernel rescales and reads its MFMA
+# results with VALU code every tile; in the VGPR form they need no moves
+# between accumulation and vector registers.
+EXTRA_FLAGS = {
+    "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -29,17 +34,41 @@ def hipcc() -> str:
     return "hipcc"
 
 
+def compile_flags(src: str) -> list:
+    """Flags for one source file (without -c / -o)."""
+    return [*HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []),
+            "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc")]
+
+
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
+    """Compile every source to an object (in parallel), then link the library."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs = []
+    for s in SOURCES:
+        src = os.path.join(HERE, "csrc", s)
+        obj = os.path.join(objdir, s + ".o")
+        cmd = [hipcc(), *compile_flags(src), "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((obj, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for obj, cmd, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            failed.append((cmd, out))
+    if failed:
+        for cmd, out in failed:
+            sys.stderr.write(" ".join(cmd) + "\n" + out)
+        raise RuntimeError(f"hipcc failed for {len(failed)} source(s)")
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc"),
-           *srcs, "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *[o for o, _, _ in procs], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
+        raise RuntimeError(f"link failed with exit code {r.returncode}")
     os.replace(tmp, OUT)
     return OUT
 

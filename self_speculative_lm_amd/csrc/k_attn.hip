@@ -6,27 +6,29 @@
 // [Notes §3.2; Digest, Method].  Query head h reads kv head h / (hq / hkv).
 //
 // bf16 kernel (gfx950 MFMA): one workgroup per (split of kv_split keys,
-// group of up to 16*WAVES*QT query vectors, sequence x kv head).  All query
-// heads of a kv head share the K/V tiles, so K [64 keys][128] and V^T
-// [128][64 keys] tiles are staged in LDS (V is cached transposed, so both
-// tiles are contiguous 16-byte loads) and read by every wave.  The tiles are
-// double-buffered: the loads of tile t+1 are in flight while tile t runs, and
-// they are unconditional (a tile never crosses the cache capacity, and the
-// cache holds finite values everywhere, so keys past a row's limit are masked
-// through their scores alone).  Each wave owns QT tiles of 16 query vectors
-// and computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16, reading every K and
-// V fragment from LDS once for its QT query tiles.  The K rows fed to the
-// MFMA are permuted so that a lane ends up holding 8 scores of one query for 8
+// group of query vectors, sequence x kv head).  All query heads of a kv head
+// share the K/V tiles, so K [64 keys][128] and V^T [128][64 keys] tiles are
+// staged in LDS (V is cached transposed, so both tiles are contiguous 16-byte
+// loads) and read by every wave that needs them.  The waves form two key
+// groups that walk alternate tiles of the split, each with its own
+// double-buffered tiles, and are merged through LDS at the end.  Tile loads
+// are unconditional (a tile never crosses the cache capacity; keys past a
+// row's limit are masked through their scores, and V past the last valid key
+// is zeroed when staged).  Each wave owns QT tiles of 16 query vectors and
+// computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16, reading every K and V
+// fragment from LDS once for its QT query tiles.  The K rows fed to the MFMA
+// are permuted so that a lane ends up holding 8 scores of one query for 8
 // consecutive keys: the softmax row statistics then need only two cross-lane
 // steps, and the same registers, rounded to fp16, are directly the B operand
 // of O^T = V^T P^T (no LDS round trip for P).  P.V runs in fp16 (V converted
 // from bf16 when staged, exact inside the fp16 range and saturated at
-// +-65504): P in [0, 1] keeps 11 significant bits instead of bf16's 8, which
-// measurably moved the logits of 4096-wide models.  Online softmax in float32
-// (exp2 with the scale folded in).  Splits write unnormalised partials
-// (O, m, l) that a combine kernel merges in split order; a launch with a
-// single split normalises in place.  A row's result depends only on its own
-// q, its keys and kv_split, not on the other rows of the launch.
+// +-65504): P keeps 11 significant bits instead of bf16's 8, which measurably
+// moved the logits of 4096-wide models.  Online softmax in float32 (exp2 with
+// the scale folded in, a lazily moved maximum, masks only on tiles that cross
+// a query's limit).  Splits write unnormalised partials (O, m, l) that a
+// combine kernel merges in split order; a launch with a single split
+// normalises in place.  A row's result depends only on its own q, its keys
+// and kv_split, not on the other rows of the launch.
 #include <math.h>
 
 #include "tri_common.h"
@@ -41,14 +43,17 @@ constexpr int KT = 64;
 constexpr int KPAD = HD + 8;  // LDS row stride (elements) of the K tile
 constexpr int VPAD = KT + 8;  // LDS row stride (elements) of the V^T tile
 
+// The first 32 bytes hold what the prologue needs before anything else (one
+// scalar load), so the sequence lookups follow it directly.
 struct AttnArgs {
-  const bf16_t* q;
-  const bf16_t* kc;
-  const bf16_t* vc;
   const int32_t* seq_start;
   const int32_t* slot_seq;
   const int32_t* row_hi;
-  int rows, hq, hkv, ctx, kv_split, nsplit;
+  int hq, hkv;
+  const bf16_t* q;
+  const bf16_t* kc;
+  const bf16_t* vc;
+  int rows, ctx, kv_split, nsplit;
   float scale_log2;
   bf16_t* out;
   float* part_o;   // [nsplit][rows][hq][HD]
@@ -59,29 +64,69 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// NT_ALL > 0: a split holds at most NT_ALL tiles and all of them are loaded at
-// once, together with the queries, before anything else (one memory round
-// trip per split, the rest is compute); NT_ALL == 0: any number of tiles,
-// double-buffered.
-template <int WAVES, int QT, int NT_ALL>
-__global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int NT = WAVES * 64;
+// Cross-lane reductions without an LDS round trip.  v_permlane16_swap
+// (v_permlane32_swap) exchanges the odd 16-lane rows (the upper 32 lanes) of
+// one register with the even rows (the lower 32 lanes) of another; fed the same
+// value twice, the two results of lane l are x[l] and x[l ^ 16] (x[l ^ 32]).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Wave-wide integer max / min: DPP inside 16-lane rows (lane ^ 1, lane ^ 2,
+// then the half-row and row mirrors), then the two swaps.
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_i32(int x) {
+  auto op = [](int u, int v) { return MAX ? max(u, v) : min(u, v); };
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = op((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  x = op((int)r[0], (int)r[1]);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// A workgroup has KW key groups of QW waves.  Every wave of a key group owns
+// QT tiles of 16 query vectors (the query slots are the same in every key
+// group); key group kg handles the tiles kg, kg + KW, kg + 2 KW, ... of the
+// split, with its own double-buffered LDS tiles staged by its own waves, and
+// the key groups' (m, l, O) are merged through LDS at the end (exactly: a key
+// group without a valid key contributes with weight exp2(-1e30 - M) = 0).
+// The tile order inside a key group, and so every rounding, depends only on
+// kv_split and KW, never on the other rows of the launch.
+template <int QW, int KW, int QT>
+__global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int GTH = QW * 64;         // threads of a key group
   constexpr int PIECES = KT * HD / 8;  // 16-byte pieces of one K (or V^T) tile
-  constexpr int PPT = PIECES / NT;     // per thread
-  constexpr int NREG = NT_ALL > 0 ? NT_ALL : 1;
-  static_assert(PIECES % NT == 0, "every thread stages the same number of pieces");
-  __shared__ __attribute__((aligned(16))) bf16_t ks[2][KT * KPAD];
-  __shared__ __attribute__((aligned(16))) _Float16 vs[2][HD * VPAD];  // V^T tile in fp16
-  __shared__ int s_maxhi;
+  constexpr int PPT = PIECES / GTH;    // per thread
+  static_assert(PIECES % GTH == 0, "every thread stages the same number of pieces");
+  __shared__ __attribute__((aligned(16))) bf16_t ks[KW * 2][KT * KPAD];
+  __shared__ __attribute__((aligned(16))) _Float16 vs[KW * 2][HD * VPAD];  // V^T tiles in fp16
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = wave / QW, qs = wave - kg * QW;  // key group, query slot
+  const int tg = tid - kg * GTH;                  // thread index inside the key group
   const int seq = blockIdx.z / a.hkv, kvh = blockIdx.z - seq * a.hkv;
   const int G = a.hq / a.hkv;
+  const int cseq = a.slot_seq ? a.slot_seq[seq] : seq;
   const int r0 = a.seq_start[seq];
   const int nq = (a.seq_start[seq + 1] - r0) * G;
-  const int qbase = blockIdx.y * (WAVES * 16 * QT);
+  const int qbase = blockIdx.y * (QW * 16 * QT);
   if (qbase >= nq) return;
   const int kbeg = blockIdx.x * a.kv_split;
-  const int cseq = a.slot_seq ? a.slot_seq[seq] : seq;
   const bf16_t* kbase = a.kc + (size_t)(cseq * a.hkv + kvh) * a.ctx * HD;
   const bf16_t* vbase = a.vc + (size_t)(cseq * a.hkv + kvh) * HD * a.ctx;
 
@@ -91,7 +136,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
     t0 = min(t0, a.ctx - KT);
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
-      const int i = tid + u * NT;
+      const int i = tg + u * GTH;
       kr[u] = ld16(kbase + (size_t)(t0 + (i >> 4)) * HD + (i & 15) * 8);
       vr[u] = ld16(vbase + (size_t)(i >> 3) * a.ctx + t0 + (i & 7) * 8);
     }
@@ -104,7 +149,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
   auto store_tile = [&](int b, const bf16x8* kr, const bf16x8* vr, int vlim) {
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
-      const int i = tid + u * NT;
+      const int i = tg + u * GTH;
       *reinterpret_cast<bf16x8*>(&ks[b][(i >> 4) * KPAD + (i & 15) * 8]) = kr[u];
       f16x8 vv;
 #pragma unroll
@@ -118,38 +163,52 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // 1. Issue the tile loads of the split (all of them, or the first) and the
-  //    query loads; they need nothing but the launch geometry.
-  bf16x8 kr[NREG][PPT], vr[NREG][PPT];
+  // 1. Loads, in the order their results are needed: the key limits of the
+  //    workgroup's rows (every wave reads all of them, lane-strided, so the
+  //    key range needs no LDS or barrier), each lane's own query limits, the
+  //    key group's first tile (a tile past the split's end re-reads a
+  //    clamped tile and is never used) and the queries.
+  constexpr int QV = QW * 16 * QT;        // query vectors of a workgroup
+  constexpr int NRL = QV / 64 + 1;        // >= rows they span / 64
+  const int qend = min(nq, qbase + QV);
+  const int rw0 = qbase / G, nrw = (qend - 1) / G - rw0 + 1;
+  int rh[NRL];
 #pragma unroll
-  for (int t = 0; t < NREG; ++t) load_tile(kbeg + t * KT, kr[t], vr[t]);
+  for (int i = 0; i < NRL; ++i) rh[i] = a.row_hi[r0 + rw0 + min(lane + 64 * i, nrw - 1)];
   const int j = lane & 15, g = lane >> 4;
+  // Query vector v of the sequence is (row r0 + v / G, head kvh * G + v % G).
+  auto qrow = [&](int q) {
+    const int v = qbase + (qs * QT + q) * 16 + j;
+    return v < nq ? r0 + v / G : r0;
+  };
+  auto qhead = [&](int q) {
+    const int v = qbase + (qs * QT + q) * 16 + j;
+    return kvh * G + (v < nq ? v % G : 0);
+  };
   bool valid[QT];
-  int row[QT], head[QT], rhi[QT];
+  int rhi[QT];
+#pragma unroll
+  for (int q = 0; q < QT; ++q) {
+    valid[q] = qbase + (qs * QT + q) * 16 + j < nq;
+    rhi[q] = a.row_hi[qrow(q)];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 ka[PPT], va[PPT];
+  load_tile(kbeg + kg * KT, ka, va);
   bf16x8 qf[QT][4];
 #pragma unroll
   for (int q = 0; q < QT; ++q) {
-    const int v = qbase + (wave * QT + q) * 16 + j;
-    valid[q] = v < nq;
-    row[q] = r0 + (valid[q] ? v / G : 0);
-    head[q] = kvh * G + (valid[q] ? v % G : 0);
-    rhi[q] = a.row_hi[row[q]];
-    const bf16_t* qp = a.q + ((size_t)row[q] * a.hq + head[q]) * HD + g * 8;
+    const bf16_t* qp = a.q + ((size_t)qrow(q) * a.hq + qhead(q)) * HD + g * 8;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) qf[q][ds] = ld16(qp + ds * 32);
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   // 2. Key range of this workgroup: up to the largest limit of its rows.
-  if (tid == 0) s_maxhi = 0;
-  __syncthreads();
-  {
-    int myhi = 0;
-    const int qend = min(nq, qbase + WAVES * 16 * QT);
-    for (int v = qbase + tid; v < qend; v += NT) myhi = max(myhi, a.row_hi[r0 + v / G]);
-    atomicMax(&s_maxhi, myhi);
-  }
-  __syncthreads();
-  const int wg_hi = s_maxhi;
+  int myhi = rh[0];
+#pragma unroll
+  for (int i = 1; i < NRL; ++i) myhi = max(myhi, rh[i]);
+  const int wg_hi = wave_reduce_i32<true>(myhi);
   if (kbeg >= wg_hi) return;
   const int kend = min(kbeg + a.kv_split, wg_hi);
   const int ntiles = (kend - kbeg + KT - 1) / KT;
@@ -167,15 +226,31 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
     m_run[q] = -1e30f;
     l_run[q] = 0.f;
   }
+  // Wave-uniform facts: whether the wave holds any valid query, and the
+  // smallest key limit of its valid queries (tiles that end at or below it
+  // need no mask).
+  int wmin = 0x7fffffff;
+  bool any_valid = false;
+#pragma unroll
+  for (int q = 0; q < QT; ++q) {
+    if (valid[q]) wmin = min(wmin, lim[q]);
+    any_valid |= valid[q];
+  }
+  wmin = wave_reduce_i32<false>(wmin);
+  const bool wave_active = __builtin_amdgcn_ballot_w64(any_valid) != 0;
 
   // One 64-key tile from LDS buffer b starting at key t0.
+  //
+  // The running maximum is lazy: the exponent base m_run moves (and O, l are
+  // rescaled) only when a score exceeds it by more than RESCALE (log2 units),
+  // so P = exp2(s * scale - m_run) <= 2^RESCALE.  O and l stay relative to
+  // the same m_run, so the normalised result is the same function; P keeps
+  // fp16's 11 significant bits at any magnitude below 65504.
+  constexpr float RESCALE = 8.f;
   auto compute = [&](int b, int t0) {
     // S^T tile t of key group m: MFMA row i loads key 32m + 8(i/4) + 4t + i%4,
     // so output lane (j, g) gets keys 32m + 8g + (4t + r) of query j.
-    float p[QT][2][8];
-    float tmax[QT];
-#pragma unroll
-    for (int q = 0; q < QT; ++q) tmax[q] = -INFINITY;
+    float sc[QT][2][8];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -191,39 +266,61 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
           for (int q = 0; q < QT; ++q) s[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[q][ds], s[q], 0, 0, 0);
         }
 #pragma unroll
-        for (int q = 0; q < QT; ++q) {
+        for (int q = 0; q < QT; ++q)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = t0 + 32 * m + 8 * g + 4 * t + r;
-            const float sv = (key < lim[q]) ? s[q][r] * a.scale_log2 : -INFINITY;
-            p[q][m][4 * t + r] = sv;
-            tmax[q] = fmaxf(tmax[q], sv);
-          }
-        }
+          for (int r = 0; r < 4; ++r) sc[q][m][4 * t + r] = s[q][r];
+      }
+    }
+    if (t0 + KT > wmin) {  // a tile that crosses some valid query's limit
+#pragma unroll
+      for (int q = 0; q < QT; ++q)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (t0 + 32 * m + 8 * g + e >= lim[q]) sc[q][m][e] = -INFINITY;
+    }
+    // Raw-score maxima (scale > 0, so the scaled maximum is the maximum
+    // scaled), then one wave-uniform decision whether any base must move.
+    float mcand[QT];
+    bool need[QT], any_need = false;
+#pragma unroll
+    for (int q = 0; q < QT; ++q) {
+      float tm = sc[q][0][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, sc[q][e >> 3][e & 7]);
+      tm = max_xor32(max_xor16(tm));
+      mcand[q] = tm * a.scale_log2;
+      need[q] = mcand[q] > m_run[q] + RESCALE;
+      any_need |= need[q];
+    }
+    // Only the queries that need it move their base (alpha = 1 exactly for
+    // the others), so a query's result does not depend on its wave mates.
+    if (__builtin_amdgcn_ballot_w64(any_need) != 0) {
+#pragma unroll
+      for (int q = 0; q < QT; ++q) {
+        const float m_new = need[q] ? mcand[q] : m_run[q];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[q] - m_new);
+        m_run[q] = m_new;
+        l_run[q] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[q][dt] *= alpha;
       }
     }
     f16x8 pb[QT][2];
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
-      float tm = tmax[q];
-      tm = fmaxf(tm, __shfl_xor(tm, 16));
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float m_new = fmaxf(m_run[q], tm);
-      const float alpha = exp2f(m_run[q] - m_new);
-      m_run[q] = m_new;
       float psum = 0.f;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = exp2f(p[q][m][e] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[q][m][e], a.scale_log2, -m_run[q]));
           psum += pv;
           pb[q][m][e] = (_Float16)pv;
         }
       }
-      l_run[q] = l_run[q] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[q][dt] *= alpha;
+      l_run[q] += psum;
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -237,51 +334,79 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // 3. Tiles: stage, then multiply.
-  if constexpr (NT_ALL > 0) {
-    // every tile of the split is already in flight (tiles past the split's
-    // end re-read a clamped tile and are never used)
-#pragma unroll
-    for (int t = 0; t < NT_ALL; ++t) {
-      if (t >= ntiles) break;
-      // buffer t&1 was last read by compute(t-2), which ended before the barrier of step t-1
-      store_tile(t & 1, kr[t], vr[t], t + 1 == ntiles ? tail : KT);
-      __syncthreads();
-      compute(t & 1, kbeg + t * KT);
-    }
-  } else {
-    // The last tile is peeled so that every prefetch in the loop is unconditional.
-    store_tile(0, kr[0], vr[0], ntiles == 1 ? tail : KT);
+  // 3. Tiles: iteration i of key group kg stages tile kg + KW i into the
+  //    group's LDS buffer i&1, issues the loads of its next tile into the
+  //    registers just staged (they are in flight during the multiply), and
+  //    multiplies.  Buffer i&1 was last read at iteration i-2, which every
+  //    wave finished before the barrier of iteration i-1.  The loads are
+  //    unconditional (the last iteration re-reads a clamped tile), so the
+  //    wait before staging covers exactly one tile.
+  const int niter = (ntiles + KW - 1) / KW;
+  for (int it = 0; it < niter; ++it) {
+    const int tile = kg + KW * it;
+    const int b = kg * 2 + (it & 1);
+    if (tile < ntiles) store_tile(b, ka, va, tile + 1 == ntiles ? tail : KT);
+    load_tile(kbeg + min(tile + KW, ntiles - 1) * KT, ka, va);
     __syncthreads();
-    int b = 0;
-    for (int t = 0; t + 1 < ntiles; ++t) {
-      load_tile(kbeg + (t + 1) * KT, kr[0], vr[0]);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the MFMAs
-      compute(b, kbeg + t * KT);
-      store_tile(b ^ 1, kr[0], vr[0], t + 2 == ntiles ? tail : KT);
-      __syncthreads();
-      b ^= 1;
+    if (tile < ntiles && wave_active) compute(b, kbeg + tile * KT);
+  }
+
+  // 4. Merge the key groups into key group 0 (per lane and query: the lanes
+  //    of one query share m_run, and l is reduced across them afterwards).
+  if constexpr (KW > 1) {
+    constexpr int NC = 34;  // O^T fragment (32 floats), m, l
+    static_assert((KW - 1) * QW * QT * NC * 64 * 4 <= (int)sizeof(ks), "merge area fits the K tiles");
+    float* mb = reinterpret_cast<float*>(&ks[0][0]);
+    __syncthreads();  // every wave is done with the tiles
+    if (kg > 0) {
+#pragma unroll
+      for (int q = 0; q < QT; ++q) {
+        float* d = mb + ((size_t)(((kg - 1) * QW + qs) * QT + q) * NC) * 64 + lane;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d[(dt * 4 + r) * 64] = oacc[q][dt][r];
+        d[32 * 64] = m_run[q];
+        d[33 * 64] = l_run[q];
+      }
     }
-    compute(b, kbeg + (ntiles - 1) * KT);
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int k2 = 1; k2 < KW; ++k2) {
+#pragma unroll
+      for (int q = 0; q < QT; ++q) {
+        const float* d = mb + ((size_t)(((k2 - 1) * QW + qs) * QT + q) * NC) * 64 + lane;
+        const float m2 = d[32 * 64], l2 = d[33 * 64];
+        const float M = fmaxf(m_run[q], m2);
+        const float w1 = __builtin_amdgcn_exp2f(m_run[q] - M), w2 = __builtin_amdgcn_exp2f(m2 - M);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[q][dt][r] = oacc[q][dt][r] * w1 + d[(dt * 4 + r) * 64] * w2;
+        l_run[q] = l_run[q] * w1 + l2 * w2;
+        m_run[q] = M;
+      }
+    }
   }
 
 #pragma unroll
   for (int q = 0; q < QT; ++q) {
     float l = l_run[q];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = sum_xor32(sum_xor16(l));
     if (!valid[q]) continue;
     // lane (j, g) holds O^T[16dt + 4g + r][query j]
     if (a.nsplit == 1) {
-      bf16_t* op = a.out + ((size_t)row[q] * a.hq + head[q]) * HD + 4 * g;
+      bf16_t* op = a.out + ((size_t)qrow(q) * a.hq + qhead(q)) * HD + 4 * g;
+      const float inv = 1.f / l;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        uint32_t lo = (uint32_t)f32_to_bf16(oacc[q][dt][0] / l) | ((uint32_t)f32_to_bf16(oacc[q][dt][1] / l) << 16);
-        uint32_t hi = (uint32_t)f32_to_bf16(oacc[q][dt][2] / l) | ((uint32_t)f32_to_bf16(oacc[q][dt][3] / l) << 16);
+        uint32_t lo = (uint32_t)f32_to_bf16(oacc[q][dt][0] * inv) | ((uint32_t)f32_to_bf16(oacc[q][dt][1] * inv) << 16);
+        uint32_t hi = (uint32_t)f32_to_bf16(oacc[q][dt][2] * inv) | ((uint32_t)f32_to_bf16(oacc[q][dt][3] * inv) << 16);
         *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(lo, hi);
       }
     } else {
-      const size_t base = ((size_t)blockIdx.x * a.rows + row[q]) * a.hq + head[q];
+      const size_t base = ((size_t)blockIdx.x * a.rows + qrow(q)) * a.hq + qhead(q);
       float* po = a.part_o + base * HD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = oacc[q][dt];
@@ -294,32 +419,40 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // Merge the split partials of one (row, head) in split order, as one online
-// pass; the partials of up to 16 splits are loaded at once.
+// pass.  The partials of up to 16 splits are loaded at once, issued together
+// with the row's key limit (indices clamped to the launch's nsplit), and only
+// the row's own splits, ceil(hi / kv_split) of them, are merged.
+// One workgroup per (row, 4 heads), one thread per output element.
 template <typename T>
-__global__ void attn_combine_kernel(const float* part_o, const float* part_ml, const int32_t* row_hi,
-                                    int rows, int hq, int hd, int kv_split, T* out) {
+__global__ __launch_bounds__(512) void attn_combine_kernel(const float* part_o, const float* part_ml,
+                                                           const int32_t* row_hi, int rows, int hq, int hd,
+                                                           int kv_split, int nsplit, T* out) {
   constexpr int B = 16;
-  const int row = blockIdx.x, head = blockIdx.y, d = threadIdx.x;
-  const int ns = (row_hi[row] + kv_split - 1) / kv_split;
+  const int row = blockIdx.x, head = blockIdx.y * 4 + (int)threadIdx.x / HD, d = threadIdx.x % HD;
+  if (head >= hq) return;
+  const int hi = row_hi[row];
   float M = -1e30f, L = 0.f, O = 0.f;
-  for (int c0 = 0; c0 < ns; c0 += B) {
+  for (int c0 = 0; c0 < nsplit; c0 += B) {
     float m[B], l[B], o[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      const size_t base = ((size_t)min(c0 + i, ns - 1) * rows + row) * hq + head;
+      const size_t base = ((size_t)min(c0 + i, nsplit - 1) * rows + row) * hq + head;
       m[i] = part_ml[base * 2];
       l[i] = part_ml[base * 2 + 1];
       o[i] = d < hd ? part_o[base * hd + d] : 0.f;
     }
+    const int ns = (hi + kv_split - 1) / kv_split;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      if (c0 + i >= ns) break;
-      const float Mn = fmaxf(M, m[i]);
-      const float wa = exp2f(M - Mn), wb = exp2f(m[i] - Mn);
-      L = L * wa + l[i] * wb;
-      O = O * wa + o[i] * wb;
-      M = Mn;
+      if (c0 + i < ns) {
+        const float Mn = fmaxf(M, m[i]);
+        const float wa = exp2f(M - Mn), wb = exp2f(m[i] - Mn);
+        L = L * wa + l[i] * wb;
+        O = O * wa + o[i] * wb;
+        M = Mn;
+      }
     }
+    if (c0 + B >= ns) break;
   }
   if (d < hd) Elem<T>::store(out, ((size_t)row * hq + head) * hd + d, O / L);
 }
@@ -376,12 +509,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, const floa
 
 int attn_pick_split(int max_ctx) {
   // keys per split for a session of max_ctx keys: the largest power of two at
-  // most max_ctx / 32, within [128, 1024].  Measured on MI355X for 33-row
-  // decode forwards (attention + combine): 600 keys 15 us with 128-key
-  // splits, 8K keys 31 us with 512, 32K keys 64 us with 1024.  A session
-  // keeps one split size, so a row's result never depends on the launch.
+  // most max_ctx / 32, within [128, 2048].  Measured on MI355X for 33-row
+  // decode forwards (attention + combine, two key groups per workgroup): 600
+  // keys 12 us with 128-key splits, 2K keys 15 us with 256, 8K keys 25 us
+  // with 512, 32K keys 51 us with 2048.  A session keeps one split size, so a
+  // row's result never depends on the launch.
   int s = 128;
-  while (s < 1024 && 2 * s <= max_ctx / 32) s *= 2;
+  while (s < 2048 && 2 * s <= max_ctx / 32) s *= 2;
   return s;
 }
 
@@ -420,26 +554,26 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   a.part_ml = L.part + np * HD;
   const int G = L.hq / L.hkv;
   const int qtiles = (L.max_rows_per_seq * G + 15) / 16;
-  // Short prefixes: 4 waves of one query tile, several query groups (more
-  // workgroups, each latency-bound); long prefixes: 8 waves of two query tiles,
-  // one group (every K/V tile read once per kv head).
-  const bool wide = qtiles > 4 && L.max_hi > 8192;
-  const int waves = wide ? 8 : 4, qt = wide ? 2 : 1;
-  const int qgroups = (qtiles + waves * qt - 1) / (waves * qt);
-  // Splits of up to 4 tiles load all their tiles at once.
-  const int nt = (L.kv_split == KT || L.kv_split == 2 * KT || L.kv_split == 4 * KT) ? L.kv_split / KT : 0;
+  // Two key groups always (the tile order inside a key group, and so the
+  // rounding, then depends only on kv_split).  Query slots per workgroup:
+  // two for short prefixes or few query tiles (more workgroups), four
+  // otherwise; two query tiles per slot for long prefixes with more than
+  // eight query tiles per kv head (each K/V tile read once per 128 query
+  // vectors).
+  const int qt = (qtiles > 8 && L.max_hi > 4096) ? 2 : 1;
+  const int qw = (qt == 1 && (qtiles <= 2 || L.max_hi <= 1536)) ? 2 : 4;
+  const int qgroups = (qtiles + qw * qt - 1) / (qw * qt);
   dim3 grid(a.nsplit, qgroups, L.n_seq * L.hkv);
-#define TRI_ATTN(W_, Q_, N_)                                                                    \
-  if (waves == W_ && qt == Q_ && nt == N_) {                                                    \
-    hipLaunchKernelGGL((attn_bf16_kernel<W_, Q_, N_>), grid, dim3(W_ * 64), 0, st, a);          \
-  }
-  TRI_ATTN(4, 1, 1) TRI_ATTN(4, 1, 2) TRI_ATTN(4, 1, 4) TRI_ATTN(4, 1, 0)
-  TRI_ATTN(8, 2, 1) TRI_ATTN(8, 2, 2) TRI_ATTN(8, 2, 4) TRI_ATTN(8, 2, 0)
-#undef TRI_ATTN
+  if (qw == 2)
+    hipLaunchKernelGGL((attn_bf16_kernel<2, 2, 1>), grid, dim3(256), 0, st, a);
+  else if (qt == 1)
+    hipLaunchKernelGGL((attn_bf16_kernel<4, 2, 1>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<4, 2, 2>), grid, dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(L.rows, L.hq), dim3(HD), 0, st, a.part_o, a.part_ml,
-                     L.row_hi, L.rows, L.hq, HD, L.kv_split, a.out);
+  hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(L.rows, (L.hq + 3) / 4), dim3(4 * HD), 0, st, a.part_o, a.part_ml,
+                     L.row_hi, L.rows, L.hq, HD, L.kv_split, a.nsplit, a.out);
   return hipGetLastError();
 }
 

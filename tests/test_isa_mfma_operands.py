@@ -5,7 +5,7 @@ to the next, this toolchain (ROCm 7.2 clang) allocated other values into the
 upper half of a live 128-bit A operand of v_mfma_f32_16x16x32_bf16 before the
 MFMA read it; the kernel then returned non-finite sums.  The kernels are
 written to avoid that shape, and this test compiles every source to assembly
-and checks, inside each basic block, that no MFMA A/B operand register tuple
+and checks (with the library's own per-source flags), inside each basic block, that no MFMA A/B operand register tuple
 is partly overwritten after being written as a whole or while live-in.
 
 Compiles only (no GPU).  Reads the assembly of code built here.
@@ -17,6 +17,8 @@ import subprocess
 import tempfile
 
 import pytest
+
+from self_speculative_lm_amd.build import compile_flags
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "self_speculative_lm_amd", "csrc")
@@ -115,9 +117,8 @@ def test_no_clobbered_mfma_operand(src):
         pytest.skip("hipcc not available")
     with tempfile.TemporaryDirectory() as td:
         out = os.path.join(td, src + ".s")
-        cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "--cuda-device-only", "-S",
-               "-o", out, os.path.join(CSRC, src)]
+        path = os.path.join(CSRC, src)
+        cmd = [hipcc, *compile_flags(path), "--cuda-device-only", "-S", "-o", out, path]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         bad, n = clobbered_operands(open(out).read())

@@ -84,21 +84,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-// Wave-wide integer max / min: DPP inside 16-lane rows (lane ^ 1, lane ^ 2,
-// then the half-row and row mirrors), then the two swaps.
-template <bool MAX>
-__device__ __forceinline__ int wave_reduce_i32(int x) {
-  auto op = [](int u, int v) { return MAX ? max(u, v) : min(u, v); };
-  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));  // row_mirror
-  auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
-  x = op((int)r[0], (int)r[1]);
-  r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
-  x = op((int)r[0], (int)r[1]);
-  return __builtin_amdgcn_readfirstlane(x);
-}
 
 // A workgroup has KW key groups of QW waves.  Every wave of a key group owns
 // QT tiles of 16 query vectors (the query slots are the same in every key
@@ -208,7 +193,7 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
   int myhi = rh[0];
 #pragma unroll
   for (int i = 1; i < NRL; ++i) myhi = max(myhi, rh[i]);
-  const int wg_hi = wave_reduce_i32<true>(myhi);
+  const int wg_hi = __builtin_amdgcn_readfirstlane(wave_max_i32(myhi));
   if (kbeg >= wg_hi) return;
   const int kend = min(kbeg + a.kv_split, wg_hi);
   const int ntiles = (kend - kbeg + KT - 1) / KT;
@@ -236,7 +221,7 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
     if (valid[q]) wmin = min(wmin, lim[q]);
     any_valid |= valid[q];
   }
-  wmin = wave_reduce_i32<false>(wmin);
+  wmin = __builtin_amdgcn_readfirstlane(wave_min_i32(wmin));
   const bool wave_active = __builtin_amdgcn_ballot_w64(any_valid) != 0;
 
   // One 64-key tile from LDS buffer b starting at key t0.

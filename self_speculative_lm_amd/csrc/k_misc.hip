@@ -40,7 +40,7 @@ __device__ __forceinline__ f32x4 slot_sum4(const float* P, int nslots, size_t st
 
 // Fixed-order sum over the blockDim.x (a multiple of 64, <= 1024) threads.
 __device__ float block_sum(float v, float* red) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  v = wave_sum_f32(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   if (lane == 0) red[wave] = v;
   __syncthreads();
@@ -65,20 +65,26 @@ __global__ void embed_kernel(const int32_t* tok, const T* E, int n_emb, int d, f
 // One 1024-thread workgroup per row, four columns per thread per pass.
 constexpr int NORM_THREADS = 1024;
 constexpr int NORM_VPT = 2;  // float4 groups per thread: d <= 1024 * 4 * 2
+// gamma is read with the row, before the reduction, and y is written with
+// one vector store per four columns.
 template <typename T>
-__global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* x, const float* P, int nslots,
-                                                                  size_t stride, int d, const float* g,
-                                                                  float eps, T* y) {
+__global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* __restrict__ x,
+                                                                  const float* __restrict__ P, int nslots,
+                                                                  size_t stride, int d,
+                                                                  const float* __restrict__ g, float eps,
+                                                                  T* __restrict__ y) {
   __shared__ float red[NORM_THREADS / 64];
   const int r = blockIdx.x, tid = threadIdx.x;
   float* xr = x + (size_t)r * d;
-  f32x4 v[NORM_VPT];
+  f32x4 v[NORM_VPT], gv[NORM_VPT];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NORM_VPT; ++i) {
     const int c = (tid + i * NORM_THREADS) * 4;
     f32x4 val = {0.f, 0.f, 0.f, 0.f};
+    gv[i] = val;
     if (c < d) {
+      gv[i] = *reinterpret_cast<const f32x4*>(g + c);
       val = *reinterpret_cast<const f32x4*>(xr + c);
       if (nslots > 0) {
         val += slot_sum4(P, nslots, stride, (size_t)r * d + c);
@@ -93,27 +99,32 @@ __global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* x, cons
 #pragma unroll
   for (int i = 0; i < NORM_VPT; ++i) {
     const int c = (tid + i * NORM_THREADS) * 4;
-    if (c < d)
-      for (int e = 0; e < 4; ++e) Elem<T>::store(y, (size_t)r * d + c + e, v[i][e] * inv * g[c + e]);
+    if (c < d) Elem<T>::store4(y, (size_t)r * d + c, v[i] * inv * gv[i]);
   }
 }
 
 // Sum the QKV slots, rotate q and k (rotate-half pairs (i, i + hd/2) by
 // pos * base^(-2i/hd), cos/sin table precomputed), store q and write k, v
 // into the cache slot of the row's position (V transposed).
-// Grid (rows, hq + 2*hkv heads), one wave per (row, head): q and k heads
-// rotate pairs (c, c + hd/2), v heads are copied to the transposed V cache.
+// Grid (rows, heads / 4), one wave per (row, head) of the hq + 2*hkv heads:
+// q and k heads rotate pairs (c, c + hd/2), v heads are copied to the
+// transposed V cache.
+constexpr int ROPE_HEADS = 4;  // waves (heads) per workgroup
 template <typename T>
-__global__ __launch_bounds__(64) void rope_kv_kernel(const float* P, int nslots, size_t stride, int hq,
-                                                     int hkv, int hd, const int32_t* row_seq,
-                                                     const int32_t* row_pos, const float* rope,
-                                                     T* qout, T* kc, T* vc, int ctx, size_t css) {
-  const int r = blockIdx.x, h = blockIdx.y;
+__global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* __restrict__ P, int nslots,
+                                                                  size_t stride, int hq, int hkv, int hd,
+                                                                  const int32_t* row_seq,
+                                                                  const int32_t* row_pos,
+                                                                  const float* __restrict__ rope,
+                                                                  T* __restrict__ qout, T* __restrict__ kc,
+                                                                  T* __restrict__ vc, int ctx, size_t css) {
+  const int r = blockIdx.x, h = blockIdx.y * ROPE_HEADS + (int)(threadIdx.x >> 6);
+  if (h >= hq + 2 * hkv) return;
   const int pos = row_pos[r], seq = row_seq[r];
   const int half = hd / 2;
   const size_t rb = (size_t)r * (hq + 2 * hkv) * hd + (size_t)h * hd;
   if (h < hq + hkv) {
-    for (int c = threadIdx.x; c < half; c += 64) {
+    for (int c = threadIdx.x & 63; c < half; c += 64) {
       const float xa = slot_sum(P, nslots, stride, rb + c);
       const float xb = slot_sum(P, nslots, stride, rb + c + half);
       const float cs = rope[((size_t)pos * half + c) * 2];
@@ -132,7 +143,7 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* P, int nslots,
     }
   } else {
     const int kh = h - hq - hkv;
-    for (int dd = threadIdx.x; dd < hd; dd += 64) {
+    for (int dd = threadIdx.x & 63; dd < hd; dd += 64) {
       const float val = slot_sum(P, nslots, stride, rb + dd);
       Elem<T>::store(vc, (size_t)seq * css + ((size_t)kh * hd + dd) * ctx + pos, val);
     }
@@ -142,8 +153,8 @@ __global__ __launch_bounds__(64) void rope_kv_kernel(const float* P, int nslots,
 // h = silu(gate) * up with gate = slots of columns [0, ffn), up = [ffn, 2 ffn);
 // one thread per four consecutive columns of one row.
 template <typename T>
-__global__ __launch_bounds__(256) void swiglu_kernel(const float* P, int nslots, size_t stride, int rows,
-                                                     int ffn, T* h) {
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ P, int nslots, size_t stride,
+                                                     int rows, int ffn, T* __restrict__ h) {
   const int q4 = ffn / 4;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * q4) return;
@@ -151,8 +162,10 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* P, int nslots,
   const size_t rb = (size_t)r * 2 * ffn;
   const f32x4 gt = slot_sum4(P, nslots, stride, rb + c);
   const f32x4 up = slot_sum4(P, nslots, stride, rb + ffn + c);
+  f32x4 o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) Elem<T>::store(h, (size_t)r * ffn + c + e, gt[e] / (1.0f + expf(-gt[e])) * up[e]);
+  for (int e = 0; e < 4; ++e) o[e] = gt[e] / (1.0f + expf(-gt[e])) * up[e];
+  Elem<T>::store4(h, (size_t)r * ffn + c, o);
 }
 
 // LoRA middle activation A o, kept only on flagged rows (zero elsewhere).
@@ -351,12 +364,12 @@ hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, 
                           void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (nslots > MAX_SLOTS) return hipErrorInvalidValue;
-  const dim3 grid(rows, hq + 2 * hkv);
+  const dim3 grid(rows, (hq + 2 * hkv + ROPE_HEADS - 1) / ROPE_HEADS);
   TRI_DISPATCH(dtype,
-               hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(64), 0, st, P, nslots, stride,
+               hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(64 * ROPE_HEADS), 0, st, P, nslots, stride,
                                   hq, hkv, hd, row_seq, row_pos, rope, static_cast<float*>(qout),
                                   static_cast<float*>(kc), static_cast<float*>(vc), ctx, css),
-               hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(64), 0, st, P, nslots,
+               hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(64 * ROPE_HEADS), 0, st, P, nslots,
                                   stride, hq, hkv, hd, row_seq, row_pos, rope,
                                   static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
                                   static_cast<bf16_t*>(vc), ctx, css));

@@ -26,16 +26,54 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
-// Element access for the two storage types.
+// Element access for the two storage types.  store4 writes four consecutive
+// elements (i % 4 == 0) with one vector store.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static float load(const float* p, size_t i) { return p[i]; }
   __device__ static void store(float* p, size_t i, float v) { p[i] = v; }
+  __device__ static void store4(float* p, size_t i, f32x4 v) { *reinterpret_cast<f32x4*>(p + i) = v; }
 };
 template <> struct Elem<bf16_t> {
   __device__ static float load(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
   __device__ static void store(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+  __device__ static void store4(bf16_t* p, size_t i, f32x4 v) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p + i) = make_uint2(lo, hi);
+  }
 };
+
+// Wave-wide all-reduce without an LDS round trip: DPP inside 16-lane rows
+// (lane ^ 1, lane ^ 2, then the half-row and row mirrors), then
+// v_permlane16_swap and v_permlane32_swap, which exchange the odd 16-lane rows
+// (the upper 32 lanes) of one register with the even rows (the lower 32
+// lanes) of another; fed the same value twice, the two results of lane l are
+// x[l] and x[l ^ 16] (x[l ^ 32]).  Every step combines a lane with a partner
+// holding the same operands, so all 64 lanes end with the same bits, in an
+// order fixed by the lane layout.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_allreduce_u32(uint32_t x, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(r[0], r[1]);
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+  return (int)wave_allreduce_u32((uint32_t)x, [](uint32_t a, uint32_t b) { return (uint32_t)max((int)a, (int)b); });
+}
+__device__ __forceinline__ int wave_min_i32(int x) {
+  return (int)wave_allreduce_u32((uint32_t)x, [](uint32_t a, uint32_t b) { return (uint32_t)min((int)a, (int)b); });
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  return __uint_as_float(wave_allreduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All are asynchronous.

@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--prompt", type=int, default=512)
     ap.add_argument("--block", type=int, default=32)
+    ap.add_argument("--max-rows", type=int, default=512,
+                    help="session rows per forward (prefill chunk size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-replay", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -154,7 +156,7 @@ def main():
     torch.cuda.empty_cache()
     prof_rounds = max(8, args.steps // 4)
     max_ctx = args.prompt + (k + 1) * (args.steps + args.warmup + prof_rounds + 2) + 64
-    sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=128, device=dev)
+    sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=args.max_rows, device=dev)
     prompt = seeded.prompt(args.prompt, shape.vocab)
     if args.calib_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)  # 256 MiB

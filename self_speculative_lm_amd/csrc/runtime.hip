@@ -111,6 +111,14 @@ Meta meta_ptrs(int32_t* base, size_t off, const MetaLayout& L) {
               b + L.seq_start, b + L.slot_seq, b + L.block_start, b + L.sidx, b + L.didx};
 }
 
+// The layout of a forward's metadata is sized by its own rows (rounded up to
+// 64, at most max_rows), so the upload of a decode forward stays small when
+// the session allows long prefill chunks.  Every user of a staged set reads
+// its layout from the session.
+MetaLayout forward_layout(int n, int max_rows, int max_batch) {
+  return meta_layout(std::min((n + 63) & ~63, max_rows), max_batch);
+}
+
 // Host-side rows of one forward.
 struct HostRows {
   std::vector<int32_t> tok, pos, hi, seq, lora, kind;
@@ -170,6 +178,7 @@ struct tri_session {
   bool lora_on = false;
   bool tracing = false;
   std::vector<TraceRec> trace;
+  MetaLayout mlay[2];                          // layout of each metadata set as last staged
   hipEvent_t meta_ev[2] = {nullptr, nullptr};  // recorded after each metadata upload
   bool meta_pending[2] = {false, false};
   int prof_class = -1;
@@ -285,7 +294,9 @@ int stage_meta(tri_session* s, int which, const HostRows& R, const std::vector<i
     HIPCHK(hipEventSynchronize(s->meta_ev[which]));
     s->meta_pending[which] = false;
   }
-  const MetaLayout ML = meta_layout(s->max_rows, s->max_batch);
+  const MetaLayout ML = forward_layout(R.n(), s->max_rows, s->max_batch);
+  if (sidx.size() > ML.didx - ML.sidx) return fail(TRI_ECAPACITY, "too many scatter entries");
+  s->mlay[which] = ML;
   Meta h = meta_ptrs(s->hints, s->o_meta[which], ML);
   const size_t n = R.n();
   memcpy(h.tok, R.tok.data(), n * 4);
@@ -305,7 +316,7 @@ int stage_meta(tri_session* s, int which, const HostRows& R, const std::vector<i
 }
 
 int upload_meta(tri_session* s, int which) {
-  const MetaLayout ML = meta_layout(s->max_rows, s->max_batch);
+  const MetaLayout& ML = s->mlay[which];
   HIPCHK(hipMemcpyAsync(s->dints + s->o_meta[which], s->hints + s->o_meta[which], ML.size * 4,
                         hipMemcpyHostToDevice, s->st));
   HIPCHK(hipEventRecord(s->meta_ev[which], s->st));
@@ -320,8 +331,7 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
   const tri_model_desc& d = m->d;
   const int n = R.n();
   if (n <= 0) return TRI_OK;
-  const MetaLayout ML = meta_layout(s->max_rows, s->max_batch);
-  Meta dm = meta_ptrs(s->dints, s->o_meta[which], ML);
+  Meta dm = meta_ptrs(s->dints, s->o_meta[which], s->mlay[which]);
   const int dt = d.dtype;
   const int hq = d.n_q_heads, hkv = d.n_kv_heads, hd = d.head_dim, D = d.d_model;
   const int qd = hq * hd;
@@ -350,7 +360,7 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
     {
       const size_t stride = (size_t)n * m->qkv_n;
       PROF(PROF_QKV, launch_gemm(dt, s->ybuf, n, D, L.qkv, m->qkv_n, m->p_qkv, s->part, stride, s->st));
-      HIPCHK(launch_rope_kv(dt, s->part, m->p_qkv.S, stride, n, hq, hkv, hd, dm.seq, dm.pos, s->rope, s->qbuf, kc,
+      HIPCHK(launch_rope_kv(dt, s->part, gemm_out_slots(dt, m->p_qkv, n, m->qkv_n, D), stride, n, hq, hkv, hd, dm.seq, dm.pos, s->rope, s->qbuf, kc,
                             vc, s->ctx, s->css, s->st));
     }
     {
@@ -375,7 +385,7 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
       a.part = static_cast<float*>(s->attn_ws);
       PROF(PROF_ATTN, launch_attn(dt, a, s->st));
     }
-    int oslots = m->p_o.S;
+    int oslots = gemm_out_slots(dt, m->p_o, n, D, qd);
     const size_t ostride = (size_t)n * D;
     {
       PROF(PROF_O, launch_gemm(dt, s->abuf, n, qd, L.o, D, m->p_o, s->part, ostride, s->st));
@@ -384,20 +394,20 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
       const int rk = d.lora_rank;
       const size_t astride = (size_t)n * rk;
       HIPCHK(launch_gemm(dt, s->abuf, n, qd, L.la, rk, m->p_la, s->part2, astride, s->st));
-      HIPCHK(launch_lora_mid(dt, s->part2, m->p_la.S, astride, n, rk, dm.lora, s->ybuf, s->st));
+      HIPCHK(launch_lora_mid(dt, s->part2, gemm_out_slots(dt, m->p_la, n, rk, qd), astride, n, rk, dm.lora, s->ybuf, s->st));
       HIPCHK(launch_gemm(dt, s->ybuf, n, rk, L.lb, D, m->p_lb, s->part + (size_t)oslots * ostride, ostride, s->st));
-      oslots += m->p_lb.S;
+      oslots += gemm_out_slots(dt, m->p_lb, n, D, rk);
     }
     HIPCHK(launch_resid_norm(dt, s->x, s->part, oslots, ostride, n, D, L.n2, d.rms_eps, s->ybuf, s->st));
     {
       const size_t stride = (size_t)n * 2 * d.d_ffn;
       PROF(PROF_GU, launch_gemm(dt, s->ybuf, n, D, L.gu, 2 * d.d_ffn, m->p_gu, s->part, stride, s->st));
-      HIPCHK(launch_swiglu(dt, s->part, m->p_gu.S, stride, n, d.d_ffn, s->ybuf, s->st));
+      HIPCHK(launch_swiglu(dt, s->part, gemm_out_slots(dt, m->p_gu, n, 2 * d.d_ffn, D), stride, n, d.d_ffn, s->ybuf, s->st));
     }
     {
       prev_stride = (size_t)n * D;
       PROF(PROF_DOWN, launch_gemm(dt, s->ybuf, n, d.d_ffn, L.down, D, m->p_down, s->part, prev_stride, s->st));
-      prev_slots = m->p_down.S;
+      prev_slots = gemm_out_slots(dt, m->p_down, n, D, d.d_ffn);
     }
   }
   if (logits_out) {
@@ -427,8 +437,7 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
 }
 
 int sample(tri_session* s, int which, const HostRows& R, const float* logits, float threshold, int status_slot) {
-  const MetaLayout ML = meta_layout(s->max_rows, s->max_batch);
-  Meta dm = meta_ptrs(s->dints, s->o_meta[which], ML);
+  Meta dm = meta_ptrs(s->dints, s->o_meta[which], s->mlay[which]);
   const int nb = R.block_start.empty() ? 0 : (int)R.block_start.size() - 1;
   HIPCHK(launch_sample_commit(logits, R.n(), s->m->d.vocab, dm.kind, dm.block_start, nb, threshold,
                               s->dints + s->o_out_tok, s->dconf, s->dints + s->o_out_commit,
@@ -547,7 +556,7 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
                   tri_seq_stats* st) {
   const int mask = s->m->d.vocab;
   const size_t na = act.size();
-  const MetaLayout ML = meta_layout(s->max_rows, s->max_batch);
+  const MetaLayout ML = forward_layout((int)na * k, s->max_rows, s->max_batch);  // the verify set's layout
   HostRows D, V;
   std::vector<int32_t> s1, d1, s2, d2;
   const int lora = s->lora_on ? 1 : 0;
@@ -578,10 +587,12 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
       d2.push_back((int32_t)(s->o_ars + j * (k + 1) + 1 + i));
     }
   }
-  Meta m0 = meta_ptrs(s->dints, s->o_meta[0], ML);
-  Meta m1 = meta_ptrs(s->dints, s->o_meta[1], ML);
+  if (V.n() != (int)na * k) return fail(TRI_EINVAL, "verify rows");
   int rc = stage_meta(s, 0, D, s1, d1);
   if (!rc) rc = stage_meta(s, 1, V, s2, d2);
+  if (rc) return rc;
+  Meta m0 = meta_ptrs(s->dints, s->o_meta[0], s->mlay[0]);
+  Meta m1 = meta_ptrs(s->dints, s->o_meta[1], s->mlay[1]);
   if (!rc) rc = upload_meta(s, 0);
   if (!rc) rc = upload_meta(s, 1);
   if (!rc) rc = forward(s, 0, D, s->logits);

@@ -149,7 +149,9 @@ def test_small_bf16_lora_lossless():
     assert err <= TOL_BF16, err
 
 
-@pytest.mark.parametrize("shape,plen,max_rows", [(seeded.TINY, 45, 8), (seeded.SMALL_BF16, 100, 16)])
+@pytest.mark.parametrize("shape,plen,max_rows", [(seeded.TINY, 45, 8), (seeded.SMALL_BF16, 100, 16),
+                                                  (seeded.SMALL_BF16, 301, 300),   # one 300-row chunk
+                                                  (seeded.SMALL_BF16, 571, 300)])  # 300 + 270 rows
 def test_prefill_in_many_chunks_matches_oracle(shape, plen, max_rows):
     """A prompt longer than max_rows is prefilled in back-to-back chunks whose
     metadata uploads are queued asynchronously (no tracing, so nothing
@@ -171,6 +173,18 @@ def test_prefill_in_many_chunks_matches_oracle(shape, plen, max_rows):
     assert err <= tol, err
     if top2_margin(o.records[-1].logits[-1]) > 2 * tol:
         assert out[0, 0] == tok[0]
+
+
+def test_small_bf16_wide_batch_teacher_forced():
+    """Ten sequences decoded together: the forwards have 330 rows, so every
+    projection, including the 1000-wide (ragged) lm_head, runs on the
+    large-M GEMM; the logits of every traced forward match the oracle."""
+    shape = seeded.SMALL_BF16_SHARP
+    prompts = [seeded.prompt(20 + 3 * i, shape.vocab, stream=20 + i) for i in range(10)]
+    _, _, sess = gpu_generate(shape, MODE_DIFFUSION, 32, 32, tau=0.7, prompts=prompts, trace=True)
+    err, tr, _ = teacher_forced_error(shape, sess)
+    assert max(len(t["logits"]) for t in tr if t["logits"] is not None) >= 256
+    assert err <= TOL_BF16 * shape.lm_head_scale, err
 
 
 def test_state_errors_and_kv_bookkeeping():

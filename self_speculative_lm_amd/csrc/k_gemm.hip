@@ -207,149 +207,131 @@ __global__ __launch_bounds__(WAVES_PER_WG * 64) void gemm_bf16_kernel(GemmArgs a
   }
 }
 
-// Large-M GEMM (prefill chunks, M > 64 rows): Y = X W^T with the arithmetic
-// intensity of M / 2 flop per weight byte, built for the MFMA units.  One
-// 256-thread workgroup per (128-row tile, 128-feature block, group of cs
-// consecutive K splits of the packed layout), writing the group's slot; four
-// waves of 64 features x 64 rows, each a 2 x 2 array of
-// v_mfma_f32_32x32x16_bf16 tiles (A = W: lane l holds feature l%32, k
-// 8(l/32)..+8; B = X^T: lane l holds row l%32, the same k; D: lane l,
-// register r holds feature 8(r/4) + 4(l/32) + r%4 of row l%32).  A stage is
-// 64 k: W as the two packed 8 KiB blocks, copied unchanged, and X with rows
-// padded to 72 elements (the B reads of a 16-lane group then hit 16 distinct
-// bank quads).  Stages travel global -> registers (a ring of R stages in
-// flight per thread, so a stage's loads are issued R - 1 stages before they
-// are needed) -> LDS (double-buffered, one barrier per stage); every W and X
-// fragment read from LDS feeds two MFMAs.  The workgroups of one feature
-// block get ids congruent modulo 8, so they run on one XCD and share its L2.
-constexpr int BIG_BM = 128;            // rows per tile
-constexpr int BIG_KST = 64;            // k per stage (two packed k-steps)
-constexpr int BIG_XPAD = BIG_KST + 8;  // LDS row stride of the X tile (elements)
-constexpr int BIG_R = 4;               // stages in flight per thread
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
+// Large-M grid: row tiles, K-split groups (one output slot each) and packed
+// splits per group.
 struct BigGrid {
-  int ntm, nyg, cs;  // row tiles, K-split groups, packed splits per group
+  int ntm, nyg, cs;
 };
 
-template <int R>
-__global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a, BigGrid bg) {
+// Large-M GEMM (prefill chunks and wide batches): the skinny kernel's
+// structure with FPW feature fragments per wave, so that MFMA operands are
+// reused in registers instead of re-read.  W fragments stream from HBM/L2
+// straight into MFMA A operands (the packed layout is already in A order), a
+// ring of D k-steps of them in flight per wave; X (MT row tiles of 16) is
+// staged in LDS per 256-wide stage, double-buffered.  Every B fragment read
+// from LDS feeds FPW MFMAs and every A fragment MT, so LDS carries one 1 KiB
+// fragment per FPW MFMAs.  A workgroup of WAVES waves covers WAVES*FPW
+// fragments (WAVES*FPW/8 packed blocks of 128 features) x MT*16 rows over a
+// group of cs consecutive K splits (output slot yg); one pass covers a whole
+// split (or an equal part of it) in straight-line code, so no fragment
+// crosses a back-edge.  The workgroups of one feature group get ids
+// congruent modulo 8, so they run on one XCD and share its L2 for W.
+template <int MT, int NCH, int D, int FPW, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGrid bg) {
+  constexpr int NT = WAVES * 64, NS = NCH * KSTEPS;
+  constexpr int BPW = WAVES * FPW / 8;           // packed blocks per workgroup
+  constexpr int XPIECES = MT * 16 * (KC / 8);    // 16-byte pieces of one X stage
+  constexpr int XPT = XPIECES / NT;
+  static_assert(XPIECES % NT == 0 && (WAVES * FPW) % 8 == 0 && 8 % FPW == 0, "shape");
+  __shared__ bf16x8 xs[2][KSTEPS][MT][64];
   const int id = blockIdx.x;
   const int q = id >> 3, per = bg.ntm * bg.nyg;
-  const int fbx = (q / per) * 8 + (id & 7), rem = q - (q / per) * per;
+  const int fgx = (q / per) * 8 + (id & 7), rem = q - (q / per) * per;  // feature group (BPW blocks)
   const int tm = rem % bg.ntm, yg = rem / bg.ntm;
-  if (fbx >= a.nfb) return;
-  __shared__ bf16x8 ws[2][2 * 512];                                          // 2 x 8 KiB per buffer
-  __shared__ __attribute__((aligned(16))) bf16_t xs[2][BIG_BM * BIG_XPAD];  // 18 KiB per buffer
+  if (fgx * BPW >= a.nfb) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wf = wave & 1, wm = wave >> 1;  // the wave's 64-feature and 64-row halves
-  const int m0 = tm * BIG_BM;
   const int G = a.nfb * a.S;
-  const int steps = a.Ks / 32;          // packed k-steps per split
-  const int kk0 = yg * bg.cs * steps;   // first k-step of the group
-  const int nst = bg.cs * steps / 2;    // stages of the group
-  const int kx0 = yg * bg.cs * a.Ks;    // first k of the group
+  const int m0 = tm * (MT * 16);
+  const int blkx = fgx * BPW + (wave * FPW) / 8;  // this wave's packed block
+  const int fg0 = (wave * FPW) % 8;               // its first fragment in the block
+  const bool wvalid = blkx < a.nfb;
+  const int bx = wvalid ? blkx : a.nfb - 1;       // clamped: loads stay inside W
+  const size_t wstep = (size_t)G * 4096;          // elements between k-steps
+  const int npass_split = a.Ks / (NCH * KC);
 
-  bf16x8 wr[R][4], xr[R][4];
-  auto load = [&](int st, bf16x8* w4, bf16x8* x4) {
-    st = min(st, nst - 1);  // past the end: re-read the last stage (never used)
+  const bf16_t* xrow[XPT];
+  int xk[XPT];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int kk = kk0 + 2 * st + b, y = kk / steps, j = kk - y * steps;
-      const bf16_t* blk = a.W + ((size_t)j * G + (size_t)y * a.nfb + fbx) * 4096;
+  for (int it = 0; it < XPT; ++it) {
+    const int i = tid + it * NT;
+    const int gg = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
+    xrow[it] = a.X + (size_t)min(m0 + r, a.M - 1) * a.K;
+    xk[it] = s * 32 + gg * 8;
+  }
+  f32x4 acc[FPW][MT];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) w4[b * 2 + u] = ld16(blk + (size_t)(tid + u * 256) * 8);
-    }
+  for (int f = 0; f < FPW; ++f)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int pc = tid + u * 256, r = pc >> 3, o = pc & 7;
-      x4[u] = ld16(a.X + (size_t)min(m0 + r, a.M - 1) * a.K + min(kx0 + st * BIG_KST + o * 8, a.K - 8));
-    }
-  };
-  auto store = [&](int b, const bf16x8* w4, const bf16x8* x4) {
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) ws[b][b2 * 512 + tid + u * 256] = w4[b2 * 2 + u];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int pc = tid + u * 256, r = pc >> 3, o = pc & 7;
-      *reinterpret_cast<bf16x8*>(&xs[b][r * BIG_XPAD + o * 8]) = x4[u];
-    }
-  };
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int tf = 0; tf < 2; ++tf)
-#pragma unroll
-    for (int tq = 0; tq < 2; ++tq)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tf][tq][r] = 0.f;
-  const int l32 = lane & 31, hi = lane >> 5;
-  auto compute = [&](int b) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {  // k 16h .. 16h + 16 of the stage
-      const int blk = h >> 1, oct = 2 * (h & 1) + hi;
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int tf = 0; tf < 2; ++tf) {
-        const int f = 64 * wf + 32 * tf + l32;  // feature inside the block
-        af[tf] = ws[b][blk * 512 + (f >> 4) * 64 + oct * 16 + (f & 15)];
-      }
-#pragma unroll
-      for (int tq = 0; tq < 2; ++tq) {
-        const int r = 64 * wm + 32 * tq + l32;
-        bfr[tq] = *reinterpret_cast<const bf16x8*>(&xs[b][r * BIG_XPAD + 16 * h + 8 * hi]);
-      }
-#pragma unroll
-      for (int tf = 0; tf < 2; ++tf)
-#pragma unroll
-        for (int tq = 0; tq < 2; ++tq)
-          acc[tf][tq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tf], bfr[tq], acc[tf][tq], 0, 0, 0);
-    }
-  };
+    for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Prologue: stages 0 .. R-1 in flight, stage 0 staged.
+  for (int pp = 0; pp < bg.cs * npass_split; ++pp) {
+    const int y = yg * bg.cs + pp / npass_split, p = pp % npass_split;
+    const int k0 = y * a.Ks + p * (NCH * KC);
+    const bf16_t* wp = a.W + ((size_t)(p * NS) * G + (size_t)y * a.nfb + bx) * 4096 + fg0 * 512 + lane * 8;
+    bf16x8 ring[D][FPW], xr[XPT];
+    auto load_x = [&](int c) {
 #pragma unroll
-  for (int i = 0; i < R; ++i) load(i, wr[i], xr[i]);
-  store(0, wr[0], xr[0]);
-  load(R, wr[0], xr[0]);
-  __syncthreads();
-  // Stage st: multiply LDS buffer st&1, stage st+1 from its register set
-  // into the other buffer (its loads were issued R - 1 stages ago), reload
-  // that set with stage st+1+R, barrier.  Unrolled by R so the register sets
-  // are fixed; iterations past nst only keep the barriers.
-  for (int s0 = 0; s0 < nst; s0 += R) {
+      for (int it = 0; it < XPT; ++it) xr[it] = ld16(xrow[it] + min(k0 + c * KC + xk[it], a.K - 8));
+    };
+    auto store_x = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int st = s0 + i;
-      if (st < nst) compute(i & 1);
-      store((i + 1) & 1, wr[(i + 1) % R], xr[(i + 1) % R]);
-      load(st + 1 + R, wr[(i + 1) % R], xr[(i + 1) % R]);
-      __syncthreads();
+      for (int it = 0; it < XPT; ++it) {
+        const int i = tid + it * NT;
+        const int gg = i & 3, r = (i >> 2) % (MT * 16), s = (i >> 2) / (MT * 16);
+        xs[b][s][r >> 4][gg * 16 + (r & 15)] = xr[it];
+      }
+    };
+    if (pp > 0) __syncthreads();  // the previous pass's last stage still reads xs
+    load_x(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+#pragma unroll
+      for (int f = 0; f < FPW; ++f) ring[i][f] = ld16(wp + (size_t)i * wstep + f * 512);
+    store_x(0);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (c + 1 < NCH) load_x(c + 1);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const int j = c * KSTEPS + s;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const bf16x8 bv = xs[c & 1][s][t][lane];
+#pragma unroll
+          for (int f = 0; f < FPW; ++f)
+            acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[j % D][f], bv, acc[f][t], 0, 0, 0);
+        }
+        if (j + D < NS) {
+#pragma unroll
+          for (int f = 0; f < FPW; ++f) ring[j % D][f] = ld16(wp + (size_t)(j + D) * wstep + f * 512);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c + 1 < NCH) {
+        store_x((c + 1) & 1);
+        __syncthreads();
+      }
     }
   }
-
+  if (!wvalid) return;
+  // D layout: lane l holds D[4*(l/16) + r][l%16] = Y[m0 + 16t + l%16][n + 4*(l/16) + r]
   float* out = a.P + (size_t)yg * a.slot_stride;
-  const int n0 = fbx * 128;
 #pragma unroll
-  for (int tf = 0; tf < 2; ++tf)
+  for (int f = 0; f < FPW; ++f) {
+    const int nn = blkx * 128 + (fg0 + f) * 16 + 4 * (lane >> 4);
 #pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      const int m = m0 + 64 * wm + 32 * tq + l32;
+    for (int t = 0; t < MT; ++t) {
+      const int m = m0 + t * 16 + (lane & 15);
       if (m >= a.M) continue;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int n = n0 + 64 * wf + 32 * tf + 8 * g4 + 4 * hi;
-        const f32x4 v = {acc[tf][tq][4 * g4], acc[tf][tq][4 * g4 + 1], acc[tf][tq][4 * g4 + 2],
-                         acc[tf][tq][4 * g4 + 3]};
-        if (n + 4 <= a.N && (a.N & 3) == 0) {
-          *reinterpret_cast<f32x4*>(out + (size_t)m * a.N + n) = v;
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (n + e < a.N) out[(size_t)m * a.N + n + e] = v[e];
-        }
+      if (nn + 4 <= a.N && (a.N & 3) == 0) {
+        *reinterpret_cast<f32x4*>(out + (size_t)m * a.N + nn) = acc[f][t];
+      } else {
+        for (int r = 0; r < 4; ++r)
+          if (nn + r < a.N) out[(size_t)m * a.N + nn + r] = acc[f][t][r];
       }
     }
+  }
 }
 
 // float32 path (small models): one thread per output, sequential K order.
@@ -468,26 +450,38 @@ hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, cons
 }
 
 // Which kernel a bf16 GEMM of M rows runs on.  The decode kernel streams W
-// once per 64-row tile; the large-M kernel once per launch but with fewer,
-// fatter workgroups.  Measured on MI355X (8B shapes): the large-M kernel is
+// once per 64-row tile; the large-M kernel once per 64-row tile too, but its
+// waves hold four fragments, so each W and X fragment feeds several MFMAs.  Measured on MI355X (8B shapes): the large-M kernel is
 // faster from 65 rows for the wide (N >= 16K) and long-K (K >= 8K) shapes and
 // from 256 rows for the others.
 bool gemm_use_big(int M, int N, int K) { return M > 64 && (M >= 256 || N >= 16384 || K >= 8192); }
 
-// Large-M grid: as few K-split groups (output slots) as keep >= 512
+// Large-M form: 8 waves x 4 fragments (512 features) x 4 row tiles (64 rows),
+// 4 k-steps in flight; measured best for the 8B shapes at 256..2048 rows
+// (up to 40% of the bf16 MFMA peak on the down projection).
+constexpr int BIGM_MT = 4, BIGM_D = 4, BIGM_FPW = 4, BIGM_WAVES = 8;
+constexpr int BIGM_BPW = BIGM_WAVES * BIGM_FPW / 8;  // packed blocks per workgroup
+
+// Large-M grid: as few K-split groups (output slots) as keep >= 192
 // workgroups in flight, otherwise one group per packed split.
 static BigGrid big_grid(const GemmPlan& p, int M, int N) {
   BigGrid g;
-  g.ntm = (M + BIG_BM - 1) / BIG_BM;
-  const int nfb8 = ((N + GROUP - 1) / GROUP + 7) / 8 * 8;
+  g.ntm = (M + BIGM_MT * 16 - 1) / (BIGM_MT * 16);
+  const int nfg8 = (((N + GROUP - 1) / GROUP + BIGM_BPW - 1) / BIGM_BPW + 7) / 8 * 8;
   g.nyg = p.S;
   for (int c = 1; c <= p.S; ++c)
-    if (p.S % c == 0 && nfb8 * g.ntm * c >= 512) {
+    if (p.S % c == 0 && nfg8 * g.ntm * c >= 192) {
       g.nyg = c;
       break;
     }
   g.cs = p.S / g.nyg;
   return g;
+}
+
+template <int NCH>
+void launch_wide(const GemmArgs& a, const BigGrid& g, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES>), dim3(a.ntiles),
+                     dim3(BIGM_WAVES * 64), 0, st, a, g);
 }
 
 int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K) {
@@ -512,8 +506,26 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
       a.S = plan.S;
       a.nfb = (N + GROUP - 1) / GROUP;
       const BigGrid g = big_grid(plan, M, N);
-      a.ntiles = (a.nfb + 7) / 8 * 8 * g.ntm * g.nyg;
-      hipLaunchKernelGGL((gemm_big_kernel<BIG_R>), dim3(a.ntiles), dim3(256), 0, st, a, g);
+      a.ntiles = ((a.nfb + BIGM_BPW - 1) / BIGM_BPW + 7) / 8 * 8 * g.ntm * g.nyg;
+      // passes as long as possible: the largest NCH <= 8 dividing the stages
+      // per split (one pass per split for every 8B/14B projection plan)
+      const int ps = plan.Ks / KC;
+      int nch = 1;
+      for (int c : {8, 6, 5, 4, 3, 2})
+        if (ps % c == 0) {
+          nch = c;
+          break;
+        }
+      switch (nch) {
+        case 1: launch_wide<1>(a, g, st); break;
+        case 2: launch_wide<2>(a, g, st); break;
+        case 3: launch_wide<3>(a, g, st); break;
+        case 4: launch_wide<4>(a, g, st); break;
+        case 5: launch_wide<5>(a, g, st); break;
+        case 6: launch_wide<6>(a, g, st); break;
+        case 8: launch_wide<8>(a, g, st); break;
+        default: return hipErrorInvalidValue;
+      }
       return hipGetLastError();
     }
     const int mt = M >= 64 ? 4 : (M + 15) / 16;

@@ -380,7 +380,13 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
       a.hd = hd;
       a.ctx = s->ctx;
       a.scale = scale;
+      // Decode forwards keep the session's split (a row's rounding then never
+      // depends on the launch).  A prefill chunk (no logits) has many rows
+      // over a short prefix: one split per 4096 keys, so short prompts need
+      // no combine.
       a.kv_split = s->kv_split;
+      if (!logits_out)
+        while (a.kv_split < 4096 && a.kv_split < max_hi) a.kv_split *= 2;
       a.out = s->abuf;
       a.part = static_cast<float*>(s->attn_ws);
       PROF(PROF_ATTN, launch_attn(dt, a, s->st));

@@ -187,6 +187,23 @@ def test_small_bf16_wide_batch_teacher_forced():
     assert err <= TOL_BF16 * shape.lm_head_scale, err
 
 
+def test_small_bf16_lora_wide_batch_lossless():
+    """Eight sequences in self-speculation with the drafter LoRA: the draft
+    forward has 264 rows, so the rank-128 LoRA projections (N = 128: most
+    waves of the large-M workgroup fall past the last feature block; K = 128:
+    one short split) run on the large-M GEMM.  Still lossless against AR, and
+    the teacher-forced logits match the oracle."""
+    shape = seeded.SMALL_BF16_LORA
+    prompts = [seeded.prompt(24 + 2 * i, shape.vocab, stream=40 + i) for i in range(8)]
+    ar, _, _ = gpu_generate(shape, MODE_AR, 12, 1, prompts=prompts)
+    ss, _, sess = gpu_generate(shape, MODE_SELFSPEC, 12, 32, prompts=prompts, lora=True, trace=True)
+    assert ss == ar
+    err, tr, _ = teacher_forced_error(shape, sess)
+    assert max(len(t["logits"]) for t in tr if t["logits"] is not None) >= 256
+    assert any(t["lora"].any() for t in tr)
+    assert err <= TOL_BF16, err
+
+
 def test_state_errors_and_kv_bookkeeping():
     import self_speculative_lm_amd as tm
     shape = seeded.TINY

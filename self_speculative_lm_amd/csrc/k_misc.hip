@@ -205,49 +205,93 @@ __device__ __forceinline__ Red red_merge(Red a, Red b) {
 
 constexpr int VCHUNK = 4096;
 
-// Stage 1: grid (chunks, rows); per chunk partial (m, s, idx).
-__global__ __launch_bounds__(256) void vocab_stage1_kernel(const float* logits, int vocab,
+// (m, s, idx) of lane ^ off, for the fixed-order wave merges below.
+__device__ __forceinline__ Red red_shfl(const Red& a, int off) {
+  Red o;
+  o.m = __shfl_xor(a.m, off);
+  o.s = __shfl_xor(a.s, off);
+  o.idx = __shfl_xor(a.idx, off);
+  return o;
+}
+// Merge over the 64 lanes (xor butterfly: every lane ends with the same
+// result; ties keep the lowest index, so the argmax does not depend on the
+// order).
+__device__ __forceinline__ Red wave_red(Red a) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) a = red_merge(a, red_shfl(a, off));
+  return a;
+}
+
+// Stage 1: grid (chunks, rows); per chunk partial (m, s, idx).  Each thread
+// reads 16 logits (four float4 when the row allows it), takes their maximum
+// first and then one sum of exp(x - m); the four waves merge through LDS.
+__global__ __launch_bounds__(256) void vocab_stage1_kernel(const float* __restrict__ logits, int vocab,
                                                            const int32_t* row_kind, Red* part,
                                                            int nchunk, int32_t* status) {
-  __shared__ Red sh[256];
-  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  __shared__ Red sh[4];
+  const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (c == 0 && r == 0 && tid == 0) *status = 0;
   if (row_kind[r] == 0) return;
   const float* lr = logits + (size_t)r * vocab;
-  Red acc{-INFINITY, 0.f, 0x7fffffff};
   const int beg = c * VCHUNK, end = min(vocab, beg + VCHUNK);
-  for (int i = beg + tid; i < end; i += 256) {
-    const float x = lr[i];
-    if (x > acc.m) {
-      acc.s = acc.s * expf(acc.m - x) + 1.0f;
-      acc.m = x;
-      acc.idx = i;
-    } else if (x != -INFINITY) {
-      acc.s += expf(x - acc.m);
+  float v[16];
+  int i0[4];
+  const bool vec = ((vocab & 3) == 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    i0[u] = beg + (u * 256 + tid) * 4;
+    if (vec && i0[u] + 4 <= end) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(lr + i0[u]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[u * 4 + e] = q[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[u * 4 + e] = i0[u] + e < end ? lr[i0[u] + e] : -INFINITY;
     }
   }
-  sh[tid] = acc;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) sh[tid] = red_merge(sh[tid], sh[tid + off]);
-    __syncthreads();
+  Red acc{-INFINITY, 0.f, 0x7fffffff};
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+    if (v[t] > acc.m) {  // increasing index order: the first maximum wins
+      acc.m = v[t];
+      acc.idx = i0[t >> 2] + (t & 3);
+    }
+  if (acc.idx != 0x7fffffff) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (v[t] != -INFINITY) acc.s += expf(v[t] - acc.m);
+  } else {
+    // no value above -inf: a NaN still poisons the sum (the row is flagged)
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (v[t] != v[t]) acc.s = v[t];
   }
-  if (tid == 0) part[(size_t)r * nchunk + c] = sh[0];
+  acc = wave_red(acc);
+  if (lane == 0) sh[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    Red t = sh[0];
+    for (int w = 1; w < 4; ++w) t = red_merge(t, sh[w]);
+    part[(size_t)r * nchunk + c] = t;
+  }
 }
 
-// Stage 2: one thread per row merges its chunks in order.
-__global__ void vocab_stage2_kernel(const Red* part, int rows, int nchunk, const int32_t* row_kind,
-                                    int32_t* out_tok, float* out_conf, int32_t* out_commit,
-                                    int32_t* status) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
+// Stage 2: one wave per row merges its chunks (lane-strided loads, then the
+// fixed wave merge).
+__global__ __launch_bounds__(64) void vocab_stage2_kernel(const Red* part, int rows, int nchunk,
+                                                          const int32_t* row_kind, int32_t* out_tok,
+                                                          float* out_conf, int32_t* out_commit,
+                                                          int32_t* status) {
+  const int r = blockIdx.x, lane = threadIdx.x;
   const int kind = row_kind[r];
   if (kind == 0) {
-    out_commit[r] = 0;
+    if (lane == 0) out_commit[r] = 0;
     return;
   }
-  Red acc = part[(size_t)r * nchunk];
-  for (int c = 1; c < nchunk; ++c) acc = red_merge(acc, part[(size_t)r * nchunk + c]);
+  Red acc{-INFINITY, 0.f, 0x7fffffff};
+  for (int c = lane; c < nchunk; c += 64) acc = red_merge(acc, part[(size_t)r * nchunk + c]);
+  acc = wave_red(acc);
+  if (lane != 0) return;
   const float conf = 1.0f / acc.s;
   const bool finite = isfinite(conf) && isfinite(acc.m) && acc.idx != 0x7fffffff;
   out_tok[r] = finite ? acc.idx : -1;
@@ -421,7 +465,7 @@ hipError_t launch_sample_commit(const float* logits, int rows, int vocab, const 
   Red* part = static_cast<Red*>(ws);
   hipLaunchKernelGGL(vocab_stage1_kernel, dim3(nchunk, rows), dim3(256), 0, st, logits, vocab, row_kind,
                      part, nchunk, out_status);
-  hipLaunchKernelGGL(vocab_stage2_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, part, rows, nchunk,
+  hipLaunchKernelGGL(vocab_stage2_kernel, dim3(rows), dim3(64), 0, st, part, rows, nchunk,
                      row_kind, out_tok, out_conf, out_commit, out_status);
   if (n_blocks > 0)
     hipLaunchKernelGGL(commit_kernel, dim3(n_blocks), dim3(64), 0, st, row_kind, block_start, threshold,

@@ -15,6 +15,7 @@ events on the session stream, and the CPU oracle timed on a bounded sample.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -117,6 +118,56 @@ def cpu_baseline(shape, prefix, k, tpr, repeats=5):
             "seconds_measured": round(total, 2)}
 
 
+def attention_alone(args):
+    """Block-causal attention alone through the C-ABI, at the attention-only
+    shapes (32 q / 8 kv heads x 128, a 32-row block attending bidirectionally
+    to itself and causally to the prefix): one JSON line per (prefix, batch)
+    with the launch time (HIP events on the launch stream, inputs resident)
+    against the HBM roofline of the K/V bytes it must read."""
+    import torch
+    import self_speculative_lm_amd as tm
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    hq, hkv, hd, nb = 32, 8, 128, 32
+    g = torch.Generator(device=dev).manual_seed(3)
+    for P in (512, 2048, 8192, 32768):
+        for b in (1, 8):
+            L = P + nb
+            ctx = (L + 63) // 64 * 64
+            kc = torch.randn((b, hkv, ctx, hd), generator=g, device=dev).to(torch.bfloat16)
+            vc = torch.randn((b, hkv, hd, ctx), generator=g, device=dev).to(torch.bfloat16)
+            q = torch.randn((b * nb, hq, hd), generator=g, device=dev).to(torch.bfloat16)
+            out = torch.empty_like(q)
+            ss = torch.arange(0, b * nb + 1, nb, dtype=torch.int32, device=dev)
+            hi = torch.full((b * nb,), L, dtype=torch.int32, device=dev)
+            ws = torch.empty(tm.block_causal_attn_ws_bytes(b * nb, hq, hd, L), dtype=torch.uint8, device=dev)
+
+            def run():
+                tm.block_causal_attn(q, kc, vc, ss, hi, out, 1.0 / math.sqrt(hd), max_rows_per_seq=nb, max_hi=L,
+                                     ws=ws)
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 50
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            kv_bytes = b * hkv * L * hd * 2 * 2
+            io_bytes = 2 * b * nb * hq * hd * 2
+            gbs = (kv_bytes + io_bytes) / (us * 1e-6) / 1e9
+            print(json.dumps({"metric": "block-causal attention alone", "prefix": P, "batch": b, "rows": b * nb,
+                              "heads": f"{hq}q/{hkv}kv x {hd}", "us": round(us, 2),
+                              "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                           "algorithmic_bytes": kv_bytes + io_bytes}}), flush=True)
+            del kc, vc, q, out, ws
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +179,8 @@ def main():
                     help="session rows per forward (prefill chunk size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-replay", action="store_true")
+    ap.add_argument("--attn", action="store_true",
+                    help="time block_causal_attn alone at the attention-only shapes instead of the decode round")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -135,6 +188,9 @@ def main():
         print("bench.py runs on exactly one GPU: the decode step is built and measured on a single "
               "MI355X (no multi-GPU path in this build).", file=sys.stderr)
         sys.exit(2)
+    if args.attn:
+        attention_alone(args)
+        return
 
     import numpy as np
     import torch

@@ -31,6 +31,9 @@
 // and kv_split, not on the other rows of the launch.
 #include <math.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "tri_common.h"
 
 namespace tri {
@@ -492,20 +495,59 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, const floa
 
 }  // namespace
 
-int attn_pick_split(int max_ctx) {
-  // keys per split for a session of max_ctx keys: the largest power of two at
-  // most max_ctx / 32, within [128, 2048].  Measured on MI355X for 33-row
-  // decode forwards (attention + combine, two key groups per workgroup): 600
-  // keys 12 us with 128-key splits, 2K keys 15 us with 256, 8K keys 25 us
-  // with 512, 32K keys 51 us with 2048.  A session keeps one split size, so a
-  // row's result never depends on the launch.
+// Launch shape: query slots per key group (qw) and query tiles per slot (qt).
+// Two slots for short prefixes or few query tiles (more workgroups), four
+// otherwise; two query tiles per slot for long prefixes with more than eight
+// query tiles per kv head (each K/V tile read once per 128 query vectors).
+// The rounding depends on neither choice.
+static void attn_shape(int qtiles, int max_hi, int* qw, int* qt) {
+  *qt = (qtiles > 8 && max_hi > 4096) ? 2 : 1;
+  *qw = (*qt == 1 && (qtiles <= 2 || max_hi <= 1536)) ? 2 : 4;
+}
+
+int attn_pick_split(int max_ctx, int n_seq) {
+  // Keys per split for a session of n_seq sequences of up to max_ctx keys:
+  // the largest power of two at most max_ctx * n_seq / 32, within
+  // [128, 2048].  Measured on MI355X for 33-row decode forwards at batch 1
+  // (attention + combine, two key groups per workgroup): 600 keys 12 us with
+  // 128-key splits, 2K keys 15 us with 256, 8K keys 25 us with 1024; more
+  // sequences give more workgroups, so longer splits.  A session keeps one
+  // split size, so a row's result never depends on the launch.
   int s = 128;
-  while (s < 2048 && 2 * s <= max_ctx / 32) s *= 2;
+  const double lim = (double)max_ctx * (n_seq > 0 ? n_seq : 1) / 32.0;
+  while (s < 2048 && 2.0 * s <= lim) s *= 2;
   return s;
 }
 
+int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int hkv) {
+  // Keys per split for one launch (the C-ABI's kv_split = 0): the power of two
+  // in [128, 4096] with the lowest modelled time.  Model, fitted to MI355X
+  // measurements at 32q/8kv heads, 32-row blocks, prefixes 512..32K, 1 and 8
+  // sequences: a workgroup costs 4 us plus 1.8 us per 128 keys it walks (two
+  // key groups of 64-key tiles), workgroups run one per CU in waves of 256,
+  // and more than one split adds a 4 us combine.
+  const int G = hkv > 0 ? hq / hkv : 1;
+  const int qtiles = std::max(1, (rows_per_seq * G + 15) / 16);
+  int qw, qt;
+  attn_shape(qtiles, max_hi, &qw, &qt);
+  const long qg = (qtiles + qw * qt - 1) / (qw * qt);
+  int best = 128;
+  double bt = 1e30;
+  for (int sp = 128; sp <= 4096; sp *= 2) {
+    const long ns = std::max(1, (max_hi + sp - 1) / sp);
+    const long nwg = ns * qg * std::max(1, n_seq) * std::max(1, hkv);
+    const double t = std::ceil(nwg / 256.0) * (4.0 + 1.8 * std::ceil(std::min(sp, std::max(max_hi, 1)) / 128.0)) +
+                     (ns > 1 ? 4.0 : 0.0);
+    if (t < bt) {
+      bt = t;
+      best = sp;
+    }
+  }
+  return best;
+}
+
 size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split) {
-  if (kv_split <= 0) kv_split = attn_pick_split(max_hi);
+  if (kv_split <= 0) kv_split = 128;  // the shortest split any pick makes: an upper bound
   const size_t ns = (size_t)((max_hi + kv_split - 1) / kv_split);
   if (ns <= 1) return 256;
   return ns * (size_t)rows * hq * (hd + 2) * sizeof(float) + 256;
@@ -540,13 +582,9 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   const int G = L.hq / L.hkv;
   const int qtiles = (L.max_rows_per_seq * G + 15) / 16;
   // Two key groups always (the tile order inside a key group, and so the
-  // rounding, then depends only on kv_split).  Query slots per workgroup:
-  // two for short prefixes or few query tiles (more workgroups), four
-  // otherwise; two query tiles per slot for long prefixes with more than
-  // eight query tiles per kv head (each K/V tile read once per 128 query
-  // vectors).
-  const int qt = (qtiles > 8 && L.max_hi > 4096) ? 2 : 1;
-  const int qw = (qt == 1 && (qtiles <= 2 || L.max_hi <= 1536)) ? 2 : 4;
+  // rounding, then depends only on kv_split).
+  int qw, qt;
+  attn_shape(qtiles, L.max_hi, &qw, &qt);
   const int qgroups = (qtiles + qw * qt - 1) / (qw * qt);
   dim3 grid(a.nsplit, qgroups, L.n_seq * L.hkv);
   if (qw == 2)

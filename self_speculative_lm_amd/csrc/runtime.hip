@@ -200,7 +200,7 @@ SessionLayout session_layout(const tri_model* m, int max_batch, int max_ctx, int
   const tri_model_desc& d = m->d;
   SessionLayout S;
   S.ctx = (max_ctx + 63) / 64 * 64;
-  S.kv_split = attn_pick_split(S.ctx);
+  S.kv_split = attn_pick_split(S.ctx, max_batch);
   S.css = (size_t)d.n_kv_heads * S.ctx * d.head_dim;
   const size_t cache_bytes = (size_t)d.n_layers * max_batch * S.css * m->esz;
   const size_t qd = (size_t)d.n_q_heads * d.head_dim;
@@ -1215,7 +1215,7 @@ int block_causal_attn(const void* q, const void* k_cache, const void* v_cache, i
   if (dtype == TRI_BF16 ? hd != 128 : (dtype == TRI_F32 ? (hd > 128 || hd <= 0) : true))
     return fail(TRI_EINVAL, "unsupported dtype/head_dim");
   if (!(scale > 0)) return fail(TRI_EINVAL, "scale must be positive");
-  if (kv_split == 0) kv_split = attn_pick_split(max_hi);
+  if (kv_split == 0) kv_split = attn_pick_split_launch(max_hi, n_seq, max_rows_per_seq, hq, hkv);
   if (kv_split < 64 || kv_split % 64) return fail(TRI_EINVAL, "kv_split must be a positive multiple of 64");
   if (ws_bytes < attn_ws_bytes(rows, hq, hd, max_hi, kv_split) || (!ws && ws_bytes))
     return fail(TRI_ECAPACITY, "workspace too small");

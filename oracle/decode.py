@@ -158,6 +158,17 @@ class OracleSession:
         self.accepts.append(a)
         return g[: a + 1]
 
+    def mixed_step(self, mode: int, k: int, lora: bool = False) -> List[int]:
+        """One step of a mixed batch (reading R19): two forwards, in which an
+        AR sequence commits a greedy token in each and a self-speculation
+        sequence runs one draft + verify round.  Sequences do not interact, so
+        a mixed batch is each sequence taking its own step."""
+        if mode == MODE_AR:
+            return self.ar_step() + self.ar_step()
+        if mode == MODE_SELFSPEC:
+            return self.selfspec_round(k, lora)
+        raise ValueError(f"mode {mode} cannot take part in a mixed step")
+
     def generate(self, mode: int, n_new: int, block: int = 32, threshold: float = 0.9,
                  lora: bool = False) -> List[int]:
         """Generate exactly ``n_new`` tokens (no EOS, overshoot truncated: R13)."""

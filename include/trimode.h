@@ -140,6 +140,46 @@ int tri_prefill(tri_session* session, int seq, const int32_t* tokens, int n);
 int tri_decode_step(tri_session* session, int mode, int block, float threshold,
                     int32_t* out_tokens, tri_seq_stats* out_stats);
 
+/* One mixed step: AR and self-speculation sequences share both forwards of a
+ * round.  The pages let one checkpoint serve AR at high concurrency and
+ * self-speculation at low [Notes §2 mode table and §11; Digest,
+ * Limitations]; a mixed step lets the two coexist in one batch.
+ * modes: host [max_batch], per sequence TRI_AR, TRI_SELFSPEC, or < 0 to leave
+ * the sequence out of this step.  Both forwards carry every stepped sequence:
+ *   TRI_SELFSPEC: the round of tri_decode_step (draft + verify, 1..k+1 tokens,
+ *                 n_forwards 2, accept_len a);
+ *   TRI_AR:       the pending rows in the first forward, the token it commits
+ *                 as one causal row in the second: 2 greedy tokens (n_forwards
+ *                 2, accept_len -1).
+ * Each sequence's tokens are those of the same mode run alone (lossless:
+ * the greedy AR continuation either way).  block in [1, 64]; out_tokens host
+ * [max_batch][block+1], -1 padded; out_stats host [max_batch] or NULL.
+ * Errors: TRI_EINVAL for a mode other than these; TRI_ESTATE for a stepped
+ * sequence that is not prefilled, or for no stepped sequence; TRI_ECAPACITY when
+ * a sequence would pass max_ctx (AR needs L+2, self-speculation L+block+1) or
+ * either forward would pass max_rows.  Synchronous. */
+int tri_decode_step_mixed(tri_session* session, const int32_t* modes, int block,
+                          int32_t* out_tokens, tri_seq_stats* out_stats);
+
+/* Mode choice by concurrency for one mixed step (host only, no device work).
+ * Chooses per sequence TRI_AR or TRI_SELFSPEC to maximise the step's expected
+ * committed tokens per millisecond:
+ *   tokens = 2 per AR sequence + expected[j] per self-speculation sequence;
+ *   time   = t(rows of the first forward) + t(rows of the second), where the
+ *            first forward has pending[j] rows per sequence (+ block for
+ *            self-speculation) and the second 1 (AR) or block rows;
+ *   t(r)   = the measured forward time: linear between the points
+ *            (grid_rows[i], grid_ms[i]), grid_ms[0] below the first point, the
+ *            line through the last two points beyond the last.
+ * grid_rows: host [n_grid], strictly increasing; grid_ms: host [n_grid] > 0.
+ * expected: host [n_seq], each sequence's expected tokens per self-speculation
+ * round, in [1, block+1] (e.g. a running mean of accept_len + 1).  pending:
+ * host [n_seq] rows >= 1, or NULL for one each.  modes: host [n_seq] out.
+ * Ties go to fewer self-speculation sequences, then to lower indices.
+ * TRI_EINVAL on a bad grid, block or expected value; nothing is written then. */
+int tri_choose_modes(const int32_t* grid_rows, const double* grid_ms, int n_grid, int n_seq,
+                     const double* expected, const int32_t* pending, int block, int32_t* modes);
+
 /* Enable/disable the draft-only o_proj LoRA (needs lora_rank > 0).  It only
  * ever applies to the [MASK] rows of self-speculation draft forwards: the AR
  * verifier is frozen [Notes §6]. */

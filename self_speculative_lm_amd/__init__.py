@@ -15,7 +15,7 @@ import numpy as np
 from ._lib import (TRI_AR, TRI_BF16, TRI_DIFFUSION, TRI_F32, TRI_SELFSPEC, ModelDesc, SeqStats, TriError,  # noqa: F401
                    check, lib)
 
-__all__ = ["Model", "Session", "block_causal_attn", "sample_commit", "verify_accept", "weight_names",
+__all__ = ["Model", "Session", "block_causal_attn", "sample_commit", "verify_accept", "weight_names", "choose_modes",
            "TriError", "TRI_AR", "TRI_DIFFUSION", "TRI_SELFSPEC", "TRI_F32", "TRI_BF16"]
 
 
@@ -132,6 +132,17 @@ class Session:
         check(lib().tri_decode_step(self.handle, mode, block, float(threshold), _ip(out), st))
         return out, [(s.n_committed, s.n_forwards, s.accept_len, s.n_flags) for s in st]
 
+    def decode_step_mixed(self, modes, block: int = 32):
+        """One mixed step; modes[b] in {TRI_AR, TRI_SELFSPEC} or < 0 (not
+        stepped).  Returns (tokens [max_batch][block+1] -1 padded, stats list)."""
+        m = _i32(modes)
+        if m.shape != (self.max_batch,):
+            raise ValueError(f"modes must have {self.max_batch} entries")
+        out = np.full((self.max_batch, block + 1), -1, dtype=np.int32)
+        st = (SeqStats * self.max_batch)()
+        check(lib().tri_decode_step_mixed(self.handle, _ip(m), block, _ip(out), st))
+        return out, [(s.n_committed, s.n_forwards, s.accept_len, s.n_flags) for s in st]
+
     def set_lora(self, enabled: bool) -> None:
         check(lib().tri_set_lora(self.handle, int(bool(enabled))))
 
@@ -202,6 +213,25 @@ class Session:
         ms, n = ctypes.c_double(), ctypes.c_int()
         check(lib().tri_profile_read(self.handle, ctypes.byref(ms), ctypes.byref(n)))
         return ms.value, n.value
+
+
+def choose_modes(grid_rows, grid_ms, expected, block: int, pending=None) -> np.ndarray:
+    """Per-sequence TRI_AR / TRI_SELFSPEC for one mixed step from a measured
+    forward-cost curve (rows -> ms) and each sequence's expected tokens per
+    self-speculation round (tri_choose_modes)."""
+    gr = _i32(grid_rows)
+    gm = np.ascontiguousarray(np.asarray(grid_ms, dtype=np.float64))
+    e = np.ascontiguousarray(np.asarray(expected, dtype=np.float64))
+    if gr.shape != gm.shape:
+        raise ValueError("grid_rows and grid_ms differ in length")
+    pd = None if pending is None else _i32(pending)
+    if pd is not None and pd.shape != e.shape:
+        raise ValueError("pending must match expected")
+    out = np.zeros(len(e), dtype=np.int32)
+    dp = ctypes.POINTER(ctypes.c_double)
+    check(lib().tri_choose_modes(_ip(gr), gm.ctypes.data_as(dp), len(gr), len(e), e.ctypes.data_as(dp),
+                                 None if pd is None else _ip(pd), block, _ip(out)))
+    return out
 
 
 # ----------------------------------------------------------- kernel-level calls

@@ -558,11 +558,25 @@ int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau
   return TRI_OK;
 }
 
-int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride, int32_t* out_tokens,
-                  tri_seq_stats* st) {
+// One round of two forwards over the stepped sequences.  spec[j] picks the
+// mode of act[j]:
+// * self-speculation: the draft forward runs the pending rows and k [MASK]
+//   rows, the verify forward the k drafts as causal rows; 1..k+1 tokens;
+// * AR (mixed steps only): the pending rows, then the row of the token the
+//   first forward committed; one greedy token per forward, 2 per step.
+// Every token that feeds the second forward moves on the device (gather
+// into the verify metadata), so the two forwards run back to back.
+int step_round(tri_session* s, const std::vector<int>& act, const std::vector<char>& spec, int k, int stride,
+               int32_t* out_tokens, tri_seq_stats* st) {
   const int mask = s->m->d.vocab;
   const size_t na = act.size();
-  const MetaLayout ML = forward_layout((int)na * k, s->max_rows, s->max_batch);  // the verify set's layout
+  int nv = 0;
+  bool any_ar = false;
+  for (size_t j = 0; j < na; ++j) {
+    nv += spec[j] ? k : 1;
+    any_ar = any_ar || !spec[j];
+  }
+  const MetaLayout ML = forward_layout(nv, s->max_rows, s->max_batch);  // the second forward's layout
   HostRows D, V;
   std::vector<int32_t> s1, d1, s2, d2;
   const int lora = s->lora_on ? 1 : 0;
@@ -570,17 +584,29 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
   for (size_t j = 0; j < na; ++j) {
     const Seq& S = s->seqs[act[j]];
     const int L = (int)S.tokens.size();
+    const int32_t ars = (int32_t)(s->o_ars + j * (k + 1));
     pending_rows(S, act[j], D, 1);
     const int g0row = D.n() - 1;
+    vrow0[j] = V.n();
+    // after the first forward: ars[j][0] = g0
+    s1.push_back((int32_t)(s->o_out_tok + g0row));
+    d1.push_back(ars);
+    if (!spec[j]) {
+      D.close_slot(act[j]);
+      V.add(0, L, L + 1, act[j], 0, 1);  // token g0, gathered after the first forward
+      V.close_slot(act[j]);
+      s1.push_back((int32_t)(s->o_out_tok + g0row));
+      d1.push_back((int32_t)(s->o_meta[1] + ML.tok + vrow0[j]));
+      s2.push_back((int32_t)(s->o_out_tok + vrow0[j]));
+      d2.push_back(ars + 1);
+      continue;
+    }
     const int mrow0 = D.n();
     for (int i = 0; i < k; ++i) D.add(mask, L + i, L + k, act[j], lora, 1);
     D.close_slot(act[j]);
-    vrow0[j] = V.n();
     for (int i = 0; i < k; ++i) V.add(0, L + i, L + i + 1, act[j], 0, 1);
     V.close_slot(act[j]);
-    // after the draft: ars[j][0] = g0; drafts[j][i] = d_i; verify token i = d_i
-    s1.push_back((int32_t)(s->o_out_tok + g0row));
-    d1.push_back((int32_t)(s->o_ars + j * (k + 1)));
+    // drafts[j][i] = d_i; verify token i = d_i
     for (int i = 0; i < k; ++i) {
       s1.push_back((int32_t)(s->o_out_tok + mrow0 + i));
       d1.push_back((int32_t)(s->o_drafts + j * k + i));
@@ -590,10 +616,10 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
     // after the verify: ars[j][1 + i] = g_{i+1}
     for (int i = 0; i < k; ++i) {
       s2.push_back((int32_t)(s->o_out_tok + vrow0[j] + i));
-      d2.push_back((int32_t)(s->o_ars + j * (k + 1) + 1 + i));
+      d2.push_back(ars + 1 + i);
     }
   }
-  if (V.n() != (int)na * k) return fail(TRI_EINVAL, "verify rows");
+  if (V.n() != nv) return fail(TRI_EINVAL, "verify rows");
   int rc = stage_meta(s, 0, D, s1, d1);
   if (!rc) rc = stage_meta(s, 1, V, s2, d2);
   if (rc) return rc;
@@ -608,7 +634,7 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
   // controlled-acceptance override: replace drafts (and verify tokens) by the reference
   for (size_t j = 0; j < na; ++j) {
     const Seq& S = s->seqs[act[j]];
-    if (S.a_star < 0) continue;
+    if (S.a_star < 0 || !spec[j]) continue;
     if (s->meta_pending[1]) {  // the verify rows' host mirror is rewritten below
       HIPCHK(hipEventSynchronize(s->meta_ev[1]));
       s->meta_pending[1] = false;
@@ -630,19 +656,31 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
   if (!rc) rc = sample(s, 1, V, s->logits, 0.f, 1);
   if (rc) return rc;
   HIPCHK(launch_scatter_gather(s->dints, m1.sidx, m1.didx, (int)s2.size(), s->dints, s->st));
+  // accept lengths for every sequence; an AR sequence's entries are not read
   HIPCHK(launch_verify_accept(s->dints + s->o_drafts, s->dints + s->o_ars, (int)na, k, s->dints + s->o_accept,
                               s->dints + s->o_committed, nullptr, s->st));
   rc = d2h_ints(s, s->o_accept, na);
   if (!rc) rc = d2h_ints(s, s->o_committed, na * (k + 1));
+  if (!rc && any_ar) rc = d2h_ints(s, s->o_ars, na * (k + 1));
   if (!rc) rc = d2h_ints(s, s->o_status, 2);
   if (rc) return rc;
   HIPCHK(hipStreamSynchronize(s->st));
-  (void)m1;
   if (s->hints[s->o_status] || s->hints[s->o_status + 1])
-    return fail(TRI_ENUMERIC, "non-finite logits in self-speculation round");
+    return fail(TRI_ENUMERIC, "non-finite logits in a self-speculation / mixed round");
   for (size_t j = 0; j < na; ++j) {
     Seq& S = s->seqs[act[j]];
     const int L = (int)S.tokens.size();
+    if (!spec[j]) {
+      const int32_t* g = s->hints + s->o_ars + j * (k + 1);
+      for (int i = 0; i < 2; ++i) {
+        S.tokens.push_back(g[i]);
+        out_tokens[(size_t)act[j] * stride + i] = g[i];
+      }
+      S.kv_len = L + 1;
+      S.written_hi = L + 1;
+      if (st) st[act[j]] = tri_seq_stats{2, 2, -1, 0};
+      continue;
+    }
     const int a = s->hints[s->o_accept + j];
     const int32_t* c = s->hints + s->o_committed + j * (k + 1);
     for (int i = 0; i <= a; ++i) {
@@ -654,6 +692,22 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
     if (st) st[act[j]] = tri_seq_stats{a + 1, 2, a, 0};
   }
   return TRI_OK;
+}
+
+int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride, int32_t* out_tokens,
+                  tri_seq_stats* st) {
+  return step_round(s, act, std::vector<char>(act.size(), 1), k, stride, out_tokens, st);
+}
+
+// Mode choice by concurrency (reading R19 of the oracle): forward cost from
+// the measured points, linear between them, the first point's time below
+// the first, the line through the last two beyond the last.
+double cost_ms(const int32_t* gr, const double* gm, int ng, double rows) {
+  if (ng == 1 || rows <= gr[0]) return gm[0];
+  for (int i = 1; i < ng; ++i)
+    if (rows <= gr[i] || i == ng - 1)
+      return gm[i - 1] + (gm[i] - gm[i - 1]) * (rows - gr[i - 1]) / (double)(gr[i] - gr[i - 1]);
+  return gm[ng - 1];
 }
 
 }  // namespace
@@ -1022,6 +1076,83 @@ int tri_decode_step(tri_session* s, int mode, int block, float threshold, int32_
     case TRI_DIFFUSION: return step_diffusion(s, act, block, threshold, stride, out_tokens, out_stats);
     default: return step_selfspec(s, act, block, stride, out_tokens, out_stats);
   }
+}
+
+int tri_decode_step_mixed(tri_session* s, const int32_t* modes, int block, int32_t* out_tokens,
+                          tri_seq_stats* out_stats) {
+  if (!s || !modes || !out_tokens) return fail(TRI_EINVAL, "null argument");
+  if (block < 1 || block > 64) return fail(TRI_EINVAL, "block %d outside [1, 64]", block);
+  std::vector<int> act;
+  std::vector<char> spec;
+  int rows1 = 0, rows2 = 0;
+  for (int b = 0; b < s->max_batch; ++b) {
+    const int md = modes[b];
+    if (md < 0) continue;
+    if (md != TRI_AR && md != TRI_SELFSPEC)
+      return fail(TRI_EINVAL, "mode %d of sequence %d cannot take part in a mixed step", md, b);
+    const Seq& S = s->seqs[b];
+    if (!S.active) return fail(TRI_ESTATE, "sequence %d is not prefilled", b);
+    const int L = (int)S.tokens.size();
+    const int pend = L - S.kv_len;
+    if (pend < 1) return fail(TRI_ESTATE, "sequence %d has no pending token (kv_len %d, L %d)", b, S.kv_len, L);
+    const bool sp = md == TRI_SELFSPEC;
+    if ((sp ? L + block + 1 : L + 2) > s->max_ctx)
+      return fail(TRI_ECAPACITY, "sequence %d would pass max_ctx %d", b, s->max_ctx);
+    rows1 += pend + (sp ? block : 0);
+    rows2 += sp ? block : 1;
+    act.push_back(b);
+    spec.push_back(sp ? 1 : 0);
+  }
+  if (act.empty()) return fail(TRI_ESTATE, "no sequence to step");
+  if (std::max(rows1, rows2) > s->max_rows)
+    return fail(TRI_ECAPACITY, "step needs %d rows, session allows %d", std::max(rows1, rows2), s->max_rows);
+  const int stride = block + 1;
+  for (size_t i = 0; i < (size_t)s->max_batch * stride; ++i) out_tokens[i] = -1;
+  if (out_stats)
+    for (int b = 0; b < s->max_batch; ++b) out_stats[b] = tri_seq_stats{0, 0, -1, 0};
+  s->ev_used = s->prof_class >= 0 ? s->ev_used : 0;
+  return step_round(s, act, spec, block, stride, out_tokens, out_stats);
+}
+
+int tri_choose_modes(const int32_t* grid_rows, const double* grid_ms, int n_grid, int n_seq, const double* expected,
+                     const int32_t* pending, int block, int32_t* modes) {
+  if (n_seq < 0 || n_grid < 1 || !grid_rows || !grid_ms) return fail(TRI_EINVAL, "bad cost grid or batch");
+  if (n_seq > 0 && (!expected || !modes)) return fail(TRI_EINVAL, "null argument");
+  if (block < 1 || block > 64) return fail(TRI_EINVAL, "block %d outside [1, 64]", block);
+  for (int i = 0; i < n_grid; ++i) {
+    if (!(grid_ms[i] > 0.0) || !std::isfinite(grid_ms[i])) return fail(TRI_EINVAL, "cost grid time %d", i);
+    if (i > 0 && grid_rows[i] <= grid_rows[i - 1]) return fail(TRI_EINVAL, "cost grid rows must increase");
+  }
+  double prows = 0;
+  for (int j = 0; j < n_seq; ++j) {
+    if (!(expected[j] >= 1.0 && expected[j] <= block + 1.0))
+      return fail(TRI_EINVAL, "expected tokens of sequence %d outside [1, block + 1]", j);
+    const int p = pending ? pending[j] : 1;
+    if (p < 1) return fail(TRI_EINVAL, "pending rows of sequence %d", j);
+    prows += p;
+  }
+  // rows depend only on how many sequences speculate, so for each count the
+  // best set is the largest expected rounds (ties: lowest index)
+  std::vector<int> order(n_seq);
+  for (int j = 0; j < n_seq; ++j) order[j] = j;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return expected[a] > expected[b]; });
+  auto rate = [&](int ns, double gain) {
+    const double tok = 2.0 * (n_seq - ns) + gain;
+    const double r1 = prows + (double)ns * block, r2 = (double)(n_seq - ns) + (double)ns * block;
+    return tok / (cost_ms(grid_rows, grid_ms, n_grid, r1) + cost_ms(grid_rows, grid_ms, n_grid, r2));
+  };
+  int best = 0;
+  double best_rate = n_seq > 0 ? rate(0, 0.0) : 0.0, gain = 0.0;
+  for (int ns = 1; ns <= n_seq; ++ns) {
+    gain += expected[order[ns - 1]];
+    const double r = rate(ns, gain);
+    if (r > best_rate) {
+      best_rate = r;
+      best = ns;
+    }
+  }
+  for (int i = 0; i < n_seq; ++i) modes[order[i]] = i < best ? TRI_SELFSPEC : TRI_AR;
+  return TRI_OK;
 }
 
 int tri_set_lora(tri_session* s, int enabled) {

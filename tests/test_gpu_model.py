@@ -204,6 +204,122 @@ def test_small_bf16_lora_wide_batch_lossless():
     assert err <= TOL_BF16, err
 
 
+def gpu_mixed(shape, prompts, schedule, block, lora=False, trace=False, max_ctx=200):
+    """Mixed steps: schedule[t][i] is the mode of sequence i at step t (-1: left out)."""
+    import self_speculative_lm_amd as tm
+    _, _, model, _ = get(shape)
+    sess = tm.Session(model, max_batch=len(prompts), max_ctx=max_ctx, max_rows=(block + 2) * len(prompts))
+    if lora:
+        sess.set_lora(True)
+    if trace:
+        sess.set_trace(True)
+    for i, p in enumerate(prompts):
+        sess.prefill(i, p)
+    outs = [[] for _ in prompts]
+    stats = []
+    for modes in schedule:
+        toks, st = sess.decode_step_mixed(modes, block)
+        stats.append(st)
+        for i in range(len(prompts)):
+            outs[i] += [int(t) for t in toks[i] if t >= 0]
+    return outs, stats, sess
+
+
+def oracle_mixed(shape, prompts, schedule, block, lora=False, max_ctx=200):
+    _, _, _, om = get(shape)
+    outs = []
+    for i, p in enumerate(prompts):
+        o = OracleSession(om, max_ctx)
+        o.prefill(p)
+        out = []
+        for modes in schedule:
+            if modes[i] >= 0:
+                out += o.mixed_step(modes[i], block, lora)
+        outs.append(out)
+    return outs
+
+
+def mixed_schedule(n_seq, n_steps, seed):
+    rng = np.random.default_rng(seed)
+    sched = []
+    for _ in range(n_steps):
+        m = rng.choice([-1, MODE_AR, MODE_SELFSPEC], size=n_seq, p=[0.15, 0.4, 0.45])
+        if (m < 0).all():
+            m[0] = MODE_AR
+        sched.append(m.astype(np.int32).tolist())
+    return sched
+
+
+def test_tiny_mixed_steps_match_oracle():
+    """AR and self-speculation sequences (and sequences left out) in the same
+    steps: every sequence commits exactly the oracle's tokens for its own
+    modes, with the per-mode stats, and every traced forward matches."""
+    shape = seeded.TINY_SHARP
+    prompts = [seeded.prompt(n, shape.vocab, stream=60 + i) for i, n in enumerate((16, 9, 23, 16))]
+    sched = mixed_schedule(len(prompts), 8, seed=5)
+    got, stats, sess = gpu_mixed(shape, prompts, sched, 8, trace=True)
+    want = oracle_mixed(shape, prompts, sched, 8)
+    assert got == want
+    for modes, st in zip(sched, stats):
+        for m, (n, f, a, _) in zip(modes, st):
+            if m == MODE_AR:
+                assert (n, f, a) == (2, 2, -1)
+            elif m == MODE_SELFSPEC:
+                assert 0 <= a <= 8 and n == a + 1 and f == 2
+            else:
+                assert (n, f) == (0, 0)
+    err, _, _ = teacher_forced_error(shape, sess, max_ctx=200)
+    assert err <= TOL_F32, err
+
+
+def test_small_bf16_lora_mixed_batch_lossless():
+    """Six sequences, AR and self-speculation with the drafter LoRA in the same
+    forwards (up to 200 rows: the large-M GEMM): every sequence commits the
+    greedy AR continuation and the traced logits match the oracle."""
+    shape = seeded.SMALL_BF16_LORA
+    prompts = [seeded.prompt(24 + 3 * i, shape.vocab, stream=80 + i) for i in range(6)]
+    sched = [[MODE_SELFSPEC, MODE_AR] * 3, [MODE_AR, MODE_SELFSPEC] * 3, [MODE_SELFSPEC] * 6,
+             [MODE_AR, -1, MODE_SELFSPEC, MODE_SELFSPEC, -1, MODE_AR]]
+    got, _, sess = gpu_mixed(shape, prompts, sched, 32, lora=True, trace=True)
+    n = min(len(g) for g in got)
+    ar, _, _ = gpu_generate(shape, MODE_AR, n, 1, prompts=prompts)
+    for i in range(len(prompts)):
+        assert got[i][:n] == ar[i], i
+    err, tr, _ = teacher_forced_error(shape, sess, max_ctx=200)
+    assert max(len(t["logits"]) for t in tr if t["logits"] is not None) >= 128
+    assert any(t["lora"].any() for t in tr)
+    assert err <= TOL_BF16, err
+
+
+def test_mixed_step_errors_leave_state_unchanged():
+    import self_speculative_lm_amd as tm
+    shape = seeded.TINY
+    _, _, model, _ = get(shape)
+    sess = tm.Session(model, max_batch=2, max_ctx=64, max_rows=16)
+    AR, SS = tm.TRI_AR, tm.TRI_SELFSPEC
+    with pytest.raises(tm.TriError) as e:
+        sess.decode_step_mixed([AR, -1], 8)
+    assert e.value.code == tm._lib.TRI_ESTATE               # not prefilled
+    sess.prefill(0, seeded.prompt(30, shape.vocab))
+    before = sess.state(0)
+    for modes, block, code in (([-1, -1], 8, tm._lib.TRI_ESTATE),          # nothing to step
+                               ([tm.TRI_DIFFUSION, -1], 8, tm._lib.TRI_EINVAL),
+                               ([AR, AR], 8, tm._lib.TRI_ESTATE),           # sequence 1 not prefilled
+                               ([SS, -1], 16, tm._lib.TRI_ECAPACITY),       # 1 + 16 rows > max_rows 16
+                               ([SS, -1], 40, tm._lib.TRI_ECAPACITY),       # 30 + 41 > max_ctx 64
+                               ([AR, -1], 0, tm._lib.TRI_EINVAL)):
+        with pytest.raises(tm.TriError) as e:
+            sess.decode_step_mixed(modes, block)
+        assert e.value.code == code, (modes, block)
+        assert sess.state(0) == before
+    with pytest.raises(ValueError):
+        sess.decode_step_mixed([AR], 8)
+    out, st = sess.decode_step_mixed([AR, -1], 8)
+    assert st[0][:2] == (2, 2) and (out[0, :2] >= 0).all() and (out[0, 2:] == -1).all()
+    toks, kv = sess.state(0)
+    assert len(toks) == 32 and kv == 31 and toks[30:] == out[0, :2].tolist()   # g1 stays pending
+
+
 def test_state_errors_and_kv_bookkeeping():
     import self_speculative_lm_amd as tm
     shape = seeded.TINY

@@ -168,6 +168,129 @@ def attention_alone(args):
             torch.cuda.empty_cache()
 
 
+def build_model(shape, dev):
+    import torch
+    import self_speculative_lm_amd as tm
+    t0 = time.time()
+    log(f"generating and uploading {shape.n_params() / 1e9:.2f}B seeded weights")
+    tensors = upload_weights(shape, dev)
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f}s")
+    model = tm.Model(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn,
+                     shape.vocab, tensors, dtype=tm.TRI_BF16)
+    del tensors  # the model holds its own packed copy
+    torch.cuda.empty_cache()
+    return model
+
+
+def step_flops(shape, rows):
+    """Algorithmic matmul flops of one decode forward over `rows` rows (every
+    projection and the lm_head once per row; attention excluded)."""
+    qd = shape.n_q_heads * shape.head_dim
+    p_layer = ((qd + 2 * shape.n_kv_heads * shape.head_dim) * shape.d_model + qd * shape.d_model
+               + 3 * shape.d_ffn * shape.d_model)
+    return 2.0 * rows * (shape.n_layers * p_layer + shape.vocab * shape.d_model)
+
+
+def concurrency_sweep(args):
+    """Mixed AR / self-speculation steps on the 8B-class decoder at 1..64
+    sequences.  First the cost of one forward is measured at row counts from 1
+    to 64 x (k+1); then for each batch n the committed tokens/s of all-AR steps,
+    all-self-speculation steps and the per-sequence choice of tri_choose_modes
+    from that curve.  Acceptance is controlled per sequence: its drafts are the
+    GPU's own greedy continuation up to a*, with a mismatch forced at a*
+    (a* cycles over the sequences), so expected tokens per round = a* + 1."""
+    import numpy as np
+    import torch
+    import seeded
+    import self_speculative_lm_amd as tm
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    shape = seeded.MODEL_8B
+    k = args.block
+    nmax = 64
+    a_cycle = [12, 6, 3, 1, 0]
+    a_star = [a_cycle[i % len(a_cycle)] for i in range(nmax)]
+    steps = 4
+    model = build_model(shape, dev)
+    n_ref = (steps + 1) * (k + 1) + 2
+    max_ctx = args.prompt + n_ref + 2 * (k + 1) + 64
+    sess = tm.Session(model, max_batch=nmax, max_ctx=max_ctx, max_rows=nmax * (k + 1), device=dev)
+    prompts = [seeded.prompt(args.prompt, shape.vocab, stream=100 + i) for i in range(nmax)]
+
+    def prefill(n):
+        for i in range(n):
+            sess.prefill(i, prompts[i])
+        torch.cuda.synchronize()
+
+    prefill(nmax)
+    # cost curve: teacher-forced forwards (full lm_head and sampling) of R rows
+    # spread over the sequences as causal rows from each pending position
+    grid = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, nmax * (k + 1)]
+    grid_ms = []
+    for R in grid:
+        per = [R // nmax + (1 if i < R % nmax else 0) for i in range(min(R, nmax))]
+        seq = np.concatenate([np.full(c, i) for i, c in enumerate(per)]).astype(np.int32)
+        pos = np.concatenate([args.prompt - 1 + np.arange(c) for c in per]).astype(np.int32)
+        tok = np.array([prompts[i][j % args.prompt] for i, c in enumerate(per) for j in range(c)], dtype=np.int32)
+        ts = []
+        for rep in range(6):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            sess.forward(seq, tok, pos, pos + 1)
+            ts.append(time.perf_counter() - t0)
+        grid_ms.append(float(np.median(ts[1:])) * 1e3)
+        log(f"forward over {R} rows: {grid_ms[-1]:.2f} ms")
+    # greedy continuations (the drafts' reference) from all-AR mixed steps
+    prefill(nmax)
+    while min(len(sess.state(i)[0]) for i in range(nmax)) < args.prompt + n_ref:
+        sess.decode_step_mixed([tm.TRI_AR] * nmax, k)
+    refs = [sess.state(i)[0] for i in range(nmax)]
+
+    def run(n, modes):
+        prefill(n)
+        full = list(modes) + [-1] * (nmax - n)
+        for i in range(n):
+            if modes[i] == tm.TRI_SELFSPEC:
+                sess.set_draft_override(i, refs[i], a_star[i])
+            else:
+                sess.set_draft_override(i, None, -1)
+        sess.decode_step_mixed(full, k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        committed = 0
+        for _ in range(steps):
+            _, st = sess.decode_step_mixed(full, k)
+            committed += sum(x[0] for x in st)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        ok = 0
+        for i in range(n):
+            got = sess.state(i)[0]
+            ok += got == refs[i][: len(got)]
+        n_ss = sum(1 for m in modes if m == tm.TRI_SELFSPEC)
+        rows1 = n + n_ss * k
+        rows2 = (n - n_ss) + n_ss * k
+        fl = steps * (step_flops(shape, rows1) + step_flops(shape, rows2))
+        return {"tok_s": round(committed / dt, 1), "ms_per_step": round(dt * 1e3 / steps, 3),
+                "n_selfspec": n_ss, "rows": [rows1, rows2], "match_ar": f"{ok}/{n}",
+                "mfma_frac": round(fl / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    for n in (1, 2, 4, 8, 16, 32, 64):
+        exp = [a_star[i] + 1.0 for i in range(n)]
+        chosen = tm.choose_modes(grid, grid_ms, exp, k).tolist()
+        res = {"metric": "mixed-step committed tokens/s, 8B-class, block 32", "batch": n,
+               "expected_tokens_per_round": exp if n <= 8 else f"a*+1 cycling {[a + 1 for a in a_cycle]}",
+               "all_ar": run(n, [tm.TRI_AR] * n), "all_selfspec": run(n, [tm.TRI_SELFSPEC] * n),
+               "chosen": run(n, chosen)}
+        print(json.dumps(res), flush=True)
+    for i in range(nmax):
+        sess.set_draft_override(i, None, -1)
+    print(json.dumps({"metric": "forward cost curve, 8B-class decode rows", "rows": grid,
+                      "ms": [round(t, 3) for t in grid_ms]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +304,8 @@ def main():
     ap.add_argument("--no-replay", action="store_true")
     ap.add_argument("--attn", action="store_true",
                     help="time block_causal_attn alone at the attention-only shapes instead of the decode round")
+    ap.add_argument("--concurrency", action="store_true",
+                    help="mixed AR / self-speculation steps at 1..64 sequences with the mode choice by concurrency")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -190,6 +315,9 @@ def main():
         sys.exit(2)
     if args.attn:
         attention_alone(args)
+        return
+    if args.concurrency:
+        concurrency_sweep(args)
         return
 
     import numpy as np
@@ -202,15 +330,7 @@ def main():
     torch.cuda.set_device(0)
     shape = seeded.MODEL_8B
     k = args.block
-    t0 = time.time()
-    log(f"generating and uploading {shape.n_params() / 1e9:.2f}B seeded weights")
-    tensors = upload_weights(shape, dev)
-    torch.cuda.synchronize()
-    log(f"weights ready in {time.time() - t0:.1f}s")
-    model = tm.Model(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn,
-                     shape.vocab, tensors, dtype=tm.TRI_BF16)
-    del tensors  # the model holds its own packed copy
-    torch.cuda.empty_cache()
+    model = build_model(shape, dev)
     prof_rounds = max(8, args.steps // 4)
     max_ctx = args.prompt + (k + 1) * (args.steps + args.warmup + prof_rounds + 2) + 64
     sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=args.max_rows, device=dev)

@@ -463,13 +463,17 @@ constexpr int BIGM_MT = 4, BIGM_D = 4, BIGM_FPW = 4, BIGM_WAVES = 8;
 constexpr int BIGM_BPW = BIGM_WAVES * BIGM_FPW / 8;  // packed blocks per workgroup
 
 // Large-M grid: as few K-split groups (output slots) as keep >= 192
-// workgroups in flight, otherwise one group per packed split.
-static BigGrid big_grid(const GemmPlan& p, int M, int N) {
+// workgroups in flight, otherwise one group per packed split.  With
+// `invariant`, always one slot per split: each split's partial sum is then
+// bit-identical to the decode kernel's (same MFMA, same k order from a zero
+// accumulator) and the consumer adds the slots in the same order, so a row's
+// result does not depend on how many rows share the launch.
+static BigGrid big_grid(const GemmPlan& p, int M, int N, bool invariant) {
   BigGrid g;
   g.ntm = (M + BIGM_MT * 16 - 1) / (BIGM_MT * 16);
   const int nfg8 = (((N + GROUP - 1) / GROUP + BIGM_BPW - 1) / BIGM_BPW + 7) / 8 * 8;
   g.nyg = p.S;
-  for (int c = 1; c <= p.S; ++c)
+  for (int c = 1; c <= p.S && !invariant; ++c)
     if (p.S % c == 0 && nfg8 * g.ntm * c >= 192) {
       g.nyg = c;
       break;
@@ -484,13 +488,13 @@ void launch_wide(const GemmArgs& a, const BigGrid& g, hipStream_t st) {
                      dim3(BIGM_WAVES * 64), 0, st, a, g);
 }
 
-int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K) {
+int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant) {
   if (dtype != TRI_BF16) return p.S;
-  return gemm_use_big(M, N, K) ? big_grid(p, M, N).nyg : p.S;
+  return gemm_use_big(M, N, K) ? big_grid(p, M, N, invariant).nyg : p.S;
 }
 
 hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, int N, const GemmPlan& plan, float* P,
-                       size_t slot_stride, hipStream_t st) {
+                       size_t slot_stride, bool invariant, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (dtype == TRI_BF16) {
     GemmArgs a;
@@ -505,7 +509,7 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
     if (gemm_use_big(M, N, K)) {
       a.S = plan.S;
       a.nfb = (N + GROUP - 1) / GROUP;
-      const BigGrid g = big_grid(plan, M, N);
+      const BigGrid g = big_grid(plan, M, N, invariant);
       a.ntiles = ((a.nfb + BIGM_BPW - 1) / BIGM_BPW + 7) / 8 * 8 * g.ntm * g.nyg;
       // passes as long as possible: the largest NCH <= 8 dividing the stages
       // per split (one pass per split for every 8B/14B projection plan)

@@ -348,6 +348,10 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
   int rc = prof_begin(s, PROF_FWD, &fslot);
   if (rc) return rc;
   const size_t layer_elems = (size_t)s->max_batch * s->css;
+  // Decode forwards (with logits) keep every row's result independent of the
+  // rows beside it, so self-speculation, AR and mixed batches of any size
+  // take the same greedy decisions; prefill chunks use the fastest slot count.
+  const bool inv = logits_out != nullptr;
   HIPCHK(launch_embed(dt, dm.tok, n, m->embed, d.vocab + 1, D, s->x, s->st));
   int prev_slots = 0;
   size_t prev_stride = 0;
@@ -359,8 +363,8 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
     HIPCHK(launch_resid_norm(dt, s->x, s->part, prev_slots, prev_stride, n, D, L.n1, d.rms_eps, s->ybuf, s->st));
     {
       const size_t stride = (size_t)n * m->qkv_n;
-      PROF(PROF_QKV, launch_gemm(dt, s->ybuf, n, D, L.qkv, m->qkv_n, m->p_qkv, s->part, stride, s->st));
-      HIPCHK(launch_rope_kv(dt, s->part, gemm_out_slots(dt, m->p_qkv, n, m->qkv_n, D), stride, n, hq, hkv, hd, dm.seq, dm.pos, s->rope, s->qbuf, kc,
+      PROF(PROF_QKV, launch_gemm(dt, s->ybuf, n, D, L.qkv, m->qkv_n, m->p_qkv, s->part, stride, inv, s->st));
+      HIPCHK(launch_rope_kv(dt, s->part, gemm_out_slots(dt, m->p_qkv, n, m->qkv_n, D, inv), stride, n, hq, hkv, hd, dm.seq, dm.pos, s->rope, s->qbuf, kc,
                             vc, s->ctx, s->css, s->st));
     }
     {
@@ -391,35 +395,35 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
       a.part = static_cast<float*>(s->attn_ws);
       PROF(PROF_ATTN, launch_attn(dt, a, s->st));
     }
-    int oslots = gemm_out_slots(dt, m->p_o, n, D, qd);
+    int oslots = gemm_out_slots(dt, m->p_o, n, D, qd, inv);
     const size_t ostride = (size_t)n * D;
     {
-      PROF(PROF_O, launch_gemm(dt, s->abuf, n, qd, L.o, D, m->p_o, s->part, ostride, s->st));
+      PROF(PROF_O, launch_gemm(dt, s->abuf, n, qd, L.o, D, m->p_o, s->part, ostride, inv, s->st));
     }
     if (any_lora) {
       const int rk = d.lora_rank;
       const size_t astride = (size_t)n * rk;
-      HIPCHK(launch_gemm(dt, s->abuf, n, qd, L.la, rk, m->p_la, s->part2, astride, s->st));
-      HIPCHK(launch_lora_mid(dt, s->part2, gemm_out_slots(dt, m->p_la, n, rk, qd), astride, n, rk, dm.lora, s->ybuf, s->st));
-      HIPCHK(launch_gemm(dt, s->ybuf, n, rk, L.lb, D, m->p_lb, s->part + (size_t)oslots * ostride, ostride, s->st));
-      oslots += gemm_out_slots(dt, m->p_lb, n, D, rk);
+      HIPCHK(launch_gemm(dt, s->abuf, n, qd, L.la, rk, m->p_la, s->part2, astride, inv, s->st));
+      HIPCHK(launch_lora_mid(dt, s->part2, gemm_out_slots(dt, m->p_la, n, rk, qd, inv), astride, n, rk, dm.lora, s->ybuf, s->st));
+      HIPCHK(launch_gemm(dt, s->ybuf, n, rk, L.lb, D, m->p_lb, s->part + (size_t)oslots * ostride, ostride, inv, s->st));
+      oslots += gemm_out_slots(dt, m->p_lb, n, D, rk, inv);
     }
     HIPCHK(launch_resid_norm(dt, s->x, s->part, oslots, ostride, n, D, L.n2, d.rms_eps, s->ybuf, s->st));
     {
       const size_t stride = (size_t)n * 2 * d.d_ffn;
-      PROF(PROF_GU, launch_gemm(dt, s->ybuf, n, D, L.gu, 2 * d.d_ffn, m->p_gu, s->part, stride, s->st));
-      HIPCHK(launch_swiglu(dt, s->part, gemm_out_slots(dt, m->p_gu, n, 2 * d.d_ffn, D), stride, n, d.d_ffn, s->ybuf, s->st));
+      PROF(PROF_GU, launch_gemm(dt, s->ybuf, n, D, L.gu, 2 * d.d_ffn, m->p_gu, s->part, stride, inv, s->st));
+      HIPCHK(launch_swiglu(dt, s->part, gemm_out_slots(dt, m->p_gu, n, 2 * d.d_ffn, D, inv), stride, n, d.d_ffn, s->ybuf, s->st));
     }
     {
       prev_stride = (size_t)n * D;
-      PROF(PROF_DOWN, launch_gemm(dt, s->ybuf, n, d.d_ffn, L.down, D, m->p_down, s->part, prev_stride, s->st));
-      prev_slots = gemm_out_slots(dt, m->p_down, n, D, d.d_ffn);
+      PROF(PROF_DOWN, launch_gemm(dt, s->ybuf, n, d.d_ffn, L.down, D, m->p_down, s->part, prev_stride, inv, s->st));
+      prev_slots = gemm_out_slots(dt, m->p_down, n, D, d.d_ffn, inv);
     }
   }
   if (logits_out) {
     HIPCHK(launch_resid_norm(dt, s->x, s->part, prev_slots, prev_stride, n, D, m->final_norm, d.rms_eps, s->ybuf,
                              s->st));
-    PROF(PROF_LM, launch_gemm(dt, s->ybuf, n, D, m->lm_head, d.vocab, m->p_lm, logits_out, (size_t)n * d.vocab, s->st));
+    PROF(PROF_LM, launch_gemm(dt, s->ybuf, n, D, m->lm_head, d.vocab, m->p_lm, logits_out, (size_t)n * d.vocab, inv, s->st));
   }
   rc = prof_end(s, PROF_FWD, fslot);
   if (rc) return rc;

@@ -291,6 +291,43 @@ def test_small_bf16_lora_mixed_batch_lossless():
     assert err <= TOL_BF16, err
 
 
+def test_small_bf16_rows_bit_identical_alone_and_in_a_wide_batch():
+    """Batch invariance across the GEMM kernels: eight sequences stepped
+    together (264 draft rows and 256 verify rows: every projection on the
+    large-M kernel) give bit-identical logits for every row, and the same
+    tokens, as each sequence stepped alone (33 / 32 rows: the decode kernel)."""
+    import self_speculative_lm_amd as tm
+    shape = seeded.SMALL_BF16
+    _, _, model, _ = get(shape)
+    prompts = [seeded.prompt(20 + 5 * i, shape.vocab, stream=120 + i) for i in range(8)]
+    sessions = []
+    for _ in range(2):
+        sess = tm.Session(model, max_batch=8, max_ctx=160, max_rows=8 * 34)
+        for i, p in enumerate(prompts):
+            sess.prefill(i, p)
+        sess.set_trace(True)
+        sessions.append(sess)
+    together, alone = sessions
+    SS = tm.TRI_SELFSPEC
+    for step in range(3):
+        out_t, _ = together.decode_step_mixed([SS] * 8, 32)
+        for i in range(8):
+            out_a, _ = alone.decode_step_mixed([SS if j == i else -1 for j in range(8)], 32)
+            assert (out_a[i] == out_t[i]).all(), (step, i)
+    tr_t, tr_a = together.trace(), alone.trace()
+    assert len(tr_a) == 8 * len(tr_t)
+    for f, rec in enumerate(tr_t):
+        assert len(rec["seq"]) >= 256
+        step, which = divmod(f, 2)
+        for i in range(8):
+            solo = tr_a[(step * 8 + i) * 2 + which]
+            rows = rec["seq"] == i
+            assert (solo["seq"] == i).all()
+            for key in ("tok", "pos", "hi"):
+                assert (rec[key][rows] == solo[key]).all()
+            assert np.array_equal(rec["logits"][rows], solo["logits"]), (f, i)
+
+
 def test_mixed_step_errors_leave_state_unchanged():
     import self_speculative_lm_amd as tm
     shape = seeded.TINY

@@ -409,7 +409,11 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
 // Merge the split partials of one (row, head) in split order, as one online
 // pass.  The partials of up to 16 splits are loaded at once, issued together
 // with the row's key limit (indices clamped to the launch's nsplit), and only
-// the row's own splits, ceil(hi / kv_split) of them, are merged.
+// the row's own splits, ceil(hi / kv_split) of them, are merged.  The merge
+// starts from the first split's partial and normalises as the unsplit
+// epilogue does (O * (1 / l)), so a row whose keys all lie in its first
+// split gets the same bits whether or not other rows of the launch need
+// more splits.
 // One workgroup per (row, 4 heads), one thread per output element.
 template <typename T>
 __global__ __launch_bounds__(512) void attn_combine_kernel(const float* part_o, const float* part_ml,
@@ -432,7 +436,11 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* part_o, 
     const int ns = (hi + kv_split - 1) / kv_split;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      if (c0 + i < ns) {
+      if (c0 + i == 0) {
+        M = m[0];
+        L = l[0];
+        O = o[0];
+      } else if (c0 + i < ns) {
         const float Mn = fmaxf(M, m[i]);
         const float wa = exp2f(M - Mn), wb = exp2f(m[i] - Mn);
         L = L * wa + l[i] * wb;
@@ -442,7 +450,8 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* part_o, 
     }
     if (c0 + B >= ns) break;
   }
-  if (d < hd) Elem<T>::store(out, ((size_t)row * hq + head) * hd + d, O / L);
+  const float inv = 1.f / L;
+  if (d < hd) Elem<T>::store(out, ((size_t)row * hq + head) * hd + d, O * inv);
 }
 
 // float32 path: one wave per (row, head), keys 64 at a time, one pass.

@@ -226,7 +226,12 @@ struct BigGrid {
 // split (or an equal part of it) in straight-line code, so no fragment
 // crosses a back-edge.  The workgroups of one feature group get ids
 // congruent modulo 8, so they run on one XCD and share its L2 for W.
-template <int MT, int NCH, int D, int FPW, int WAVES>
+//
+// CHAIN: each K split of the group is accumulated from zero and the splits'
+// partials are added in split order in a second register set, which is
+// exactly what a consumer does with one slot per split: the single slot then
+// holds the decode kernel's bits (batch-invariant outputs in one slot).
+template <int MT, int NCH, int D, int FPW, int WAVES, bool CHAIN>
 __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGrid bg) {
   constexpr int NT = WAVES * 64, NS = NCH * KSTEPS;
   constexpr int BPW = WAVES * FPW / 8;           // packed blocks per workgroup
@@ -259,6 +264,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGr
     xk[it] = s * 32 + gg * 8;
   }
   f32x4 acc[FPW][MT];
+  f32x4 tot[CHAIN ? FPW : 1][CHAIN ? MT : 1];
 #pragma unroll
   for (int f = 0; f < FPW; ++f)
 #pragma unroll
@@ -266,6 +272,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGr
 
   for (int pp = 0; pp < bg.cs * npass_split; ++pp) {
     const int y = yg * bg.cs + pp / npass_split, p = pp % npass_split;
+    if (CHAIN && pp > 0 && p == 0) {  // split y - 1 is complete: add its partial in split order
+#pragma unroll
+      for (int f = 0; f < FPW; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          tot[CHAIN ? f : 0][CHAIN ? t : 0] = pp == npass_split ? acc[f][t] : tot[CHAIN ? f : 0][CHAIN ? t : 0] + acc[f][t];
+          acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     const int k0 = y * a.Ks + p * (NCH * KC);
     const bf16_t* wp = a.W + ((size_t)(p * NS) * G + (size_t)y * a.nfb + bx) * 4096 + fg0 * 512 + lane * 8;
     bf16x8 ring[D][FPW], xr[XPT];
@@ -315,6 +330,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGr
     }
   }
   if (!wvalid) return;
+  if (CHAIN && bg.cs > 1) {
+#pragma unroll
+    for (int f = 0; f < FPW; ++f)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[f][t] = tot[CHAIN ? f : 0][CHAIN ? t : 0] + acc[f][t];
+  }
   // D layout: lane l holds D[4*(l/16) + r][l%16] = Y[m0 + 16t + l%16][n + 4*(l/16) + r]
   float* out = a.P + (size_t)yg * a.slot_stride;
 #pragma unroll
@@ -464,28 +485,35 @@ constexpr int BIGM_BPW = BIGM_WAVES * BIGM_FPW / 8;  // packed blocks per workgr
 
 // Large-M grid: as few K-split groups (output slots) as keep >= 192
 // workgroups in flight, otherwise one group per packed split.  With
-// `invariant`, always one slot per split: each split's partial sum is then
-// bit-identical to the decode kernel's (same MFMA, same k order from a zero
-// accumulator) and the consumer adds the slots in the same order, so a row's
-// result does not depend on how many rows share the launch.
+// `invariant` a row's result must not depend on how many rows share the
+// launch: each split's partial is bit-identical to the decode kernel's (same
+// MFMA, same k order from a zero accumulator) and consumers add slots in
+// order, so either one slot per split, or one slot for all splits with the
+// partials chained in split order (CHAIN); groups of some splits would add
+// in a different order.
 static BigGrid big_grid(const GemmPlan& p, int M, int N, bool invariant) {
   BigGrid g;
   g.ntm = (M + BIGM_MT * 16 - 1) / (BIGM_MT * 16);
   const int nfg8 = (((N + GROUP - 1) / GROUP + BIGM_BPW - 1) / BIGM_BPW + 7) / 8 * 8;
   g.nyg = p.S;
-  for (int c = 1; c <= p.S && !invariant; ++c)
+  for (int c = 1; c <= p.S; ++c)
     if (p.S % c == 0 && nfg8 * g.ntm * c >= 192) {
       g.nyg = c;
       break;
     }
+  if (invariant && g.nyg != 1) g.nyg = p.S;
   g.cs = p.S / g.nyg;
   return g;
 }
 
 template <int NCH>
-void launch_wide(const GemmArgs& a, const BigGrid& g, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES>), dim3(a.ntiles),
-                     dim3(BIGM_WAVES * 64), 0, st, a, g);
+void launch_wide(const GemmArgs& a, const BigGrid& g, bool chain, hipStream_t st) {
+  if (chain)
+    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, true>), dim3(a.ntiles),
+                       dim3(BIGM_WAVES * 64), 0, st, a, g);
+  else
+    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, false>), dim3(a.ntiles),
+                       dim3(BIGM_WAVES * 64), 0, st, a, g);
 }
 
 int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant) {
@@ -520,14 +548,15 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
           nch = c;
           break;
         }
+      const bool chain = invariant && g.cs > 1;
       switch (nch) {
-        case 1: launch_wide<1>(a, g, st); break;
-        case 2: launch_wide<2>(a, g, st); break;
-        case 3: launch_wide<3>(a, g, st); break;
-        case 4: launch_wide<4>(a, g, st); break;
-        case 5: launch_wide<5>(a, g, st); break;
-        case 6: launch_wide<6>(a, g, st); break;
-        case 8: launch_wide<8>(a, g, st); break;
+        case 1: launch_wide<1>(a, g, chain, st); break;
+        case 2: launch_wide<2>(a, g, chain, st); break;
+        case 3: launch_wide<3>(a, g, chain, st); break;
+        case 4: launch_wide<4>(a, g, chain, st); break;
+        case 5: launch_wide<5>(a, g, chain, st); break;
+        case 6: launch_wide<6>(a, g, chain, st); break;
+        case 8: launch_wide<8>(a, g, chain, st); break;
         default: return hipErrorInvalidValue;
       }
       return hipGetLastError();

@@ -124,6 +124,42 @@ def test_block_causal_attn_row_independent_of_batch(prefix, nrows, kv_split):
     assert torch.equal(pair[0], full[nrows - 1]) and torch.equal(pair[1], full[0])
 
 
+@pytest.mark.parametrize("short,long_,kv_split", [(40, 700, 256), (100, 3000, 128)])
+def test_block_causal_attn_short_row_same_bits_beside_a_long_one(short, long_, kv_split):
+    """A sequence whose keys fit in one split gets the same bits alone (one
+    split: the kernel normalises in its epilogue) and beside a sequence that
+    needs several splits (the launch then merges split partials for every
+    row, one partial for the short sequence's rows)."""
+    import torch
+    import self_speculative_lm_amd as tm
+    hq, hkv, hd, nr = 32, 8, 128, 8
+    L = long_ + nr
+    ctx = (L + 63) // 64 * 64
+    q, k, v = seeded.attention_operands(nr, long_, hq, hkv, hd, batch=2, bf16=True, seed=21)
+    kc = torch.zeros((2, hkv, ctx, hd), dtype=torch.bfloat16)
+    vc = torch.zeros((2, hkv, hd, ctx), dtype=torch.bfloat16)
+    kc[:, :, :L] = torch.from_numpy(k).permute(0, 2, 1, 3).to(torch.bfloat16)
+    vc[:, :, :, :L] = torch.from_numpy(v).permute(0, 2, 3, 1).to(torch.bfloat16)
+    kc, vc = kc.cuda(), vc.cuda()
+    tq = torch.from_numpy(q.reshape(2 * nr, hq, hd)).to(torch.bfloat16).cuda()
+    his_a = [short - nr + i + 1 for i in range(nr)]          # sequence 0: keys [0, short)
+    his_b = [long_ + i + 1 for i in range(nr)]               # sequence 1: several splits
+    assert max(his_a) <= kv_split < max(his_b)
+
+    def run(n_seq, his, kc_, vc_, qq):
+        out = torch.zeros((len(his), hq, hd), dtype=torch.bfloat16, device="cuda")
+        ss = torch.tensor([nr * i for i in range(n_seq + 1)], dtype=torch.int32, device="cuda")
+        hi = torch.tensor(his, dtype=torch.int32, device="cuda")
+        tm.block_causal_attn(qq, kc_, vc_, ss, hi, out, 1.0 / math.sqrt(hd), max_rows_per_seq=nr,
+                             max_hi=max(his), kv_split=kv_split)
+        torch.cuda.synchronize()
+        return out.cpu()
+
+    both = run(2, his_a + his_b, kc, vc, tq)
+    alone = run(1, his_a, kc[:1].contiguous(), vc[:1].contiguous(), tq[:nr].contiguous())
+    assert torch.equal(alone, both[:nr])
+
+
 @pytest.mark.parametrize("prefixes,nrows,hq,hkv,hd,causal", [
     ([0], [8], 4, 4, 32, False), ([50], [9], 4, 4, 32, True), ([20, 70], [9, 16], 4, 2, 64, False),
     ([100], [3], 2, 1, 128, False),

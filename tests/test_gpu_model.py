@@ -328,6 +328,29 @@ def test_small_bf16_rows_bit_identical_alone_and_in_a_wide_batch():
             assert np.array_equal(rec["logits"][rows], solo["logits"]), (f, i)
 
 
+def test_small_bf16_1500_rows_bit_identical_to_50_row_chunks():
+    """Batch invariance where the large-M GEMM keeps one slot for several K
+    splits (the down projection's two splits chained in split order, at
+    1500 rows): a 1500-row teacher-forced forward gives logits bit-identical
+    to the same rows run as thirty 50-row forwards on the decode kernel."""
+    import torch
+    import self_speculative_lm_amd as tm
+    shape = seeded.SMALL_BF16
+    _, _, model, _ = get(shape)
+    n, c = 1500, 50
+    toks = seeded.prompt(n, shape.vocab, stream=140)
+    pos = np.arange(n, dtype=np.int32)
+    seq = np.zeros(n, dtype=np.int32)
+    sess = tm.Session(model, max_batch=1, max_ctx=n + 64, max_rows=n)
+    big = torch.empty((n, shape.vocab), dtype=torch.float32, device="cuda")
+    sess.forward(seq, toks, pos, pos + 1, logits=big)
+    small = torch.empty((c, shape.vocab), dtype=torch.float32, device="cuda")
+    for i in range(0, n, c):
+        sess.forward(seq[i:i + c], toks[i:i + c], pos[i:i + c], pos[i:i + c] + 1, logits=small)
+        torch.cuda.synchronize()
+        assert torch.equal(big[i:i + c], small), i
+
+
 def test_mixed_step_errors_leave_state_unchanged():
     import self_speculative_lm_amd as tm
     shape = seeded.TINY

@@ -94,7 +94,7 @@ const char* tri_last_error(void);
  * copies are done: the caller may then free the original weights; model_buf
  * must stay alive and unchanged until tri_model_destroy.  bf16 models need d,
  * hq*hd, hkv*hd, ffn and r to be multiples of 64 and head_dim == 128; float32
- * models need head_dim <= 128; d and ffn are multiples of 4, d <= 8192.
+ * models need head_dim <= 128; d is a multiple of 4 and ffn of 16, d <= 8192.
  * ------------------------------------------------------------------------ */
 int tri_model_bytes(const tri_model_desc* desc, size_t* bytes);
 int tri_model_create(const tri_model_desc* desc, const void* const* weights, int n_weights,

@@ -47,6 +47,7 @@ struct GemmArgs {
   int nfb, ntiles;  // feature blocks; tiles = (M tiles) x nfb x S
   float* P;
   size_t slot_stride;
+  bf16_t* H;  // SwiGLU epilogue output [M][N/2] (gate/up projection only)
 };
 
 __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
@@ -61,8 +62,18 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
 // every k-step the workgroups of a launch read one contiguous window: measured
 // on MI355X this sustains the linear-read rate, whereas one contiguous region
 // per workgroup fell about 10% short.  K is zero-padded to S*Ks.
+// With `il`, the two segments (gate and up, r0 rows each) interleave in
+// groups of 16 rows: packed rows [32j, 32j+16) are segment 0's rows
+// [16j, 16j+16) and [32j+16, 32j+32) segment 1's, so one MFMA fragment pair
+// holds matching gate and up features.
+__device__ __forceinline__ int pack_row(int row, int r0, bool il) {
+  if (!il) return row;
+  const int j = row >> 4, w = row & 15;
+  return (j & 1) ? r0 + (j >> 1) * 16 + w : (j >> 1) * 16 + w;
+}
+
 __global__ void pack_bf16_kernel(const bf16_t* w0, const bf16_t* w1, const bf16_t* w2, int r0, int r1, int N,
-                                 int K, int nfb, int S, int steps, size_t npieces, bf16_t* dst) {
+                                 int K, int nfb, int S, int steps, size_t npieces, bool il, bf16_t* dst) {
   const int G = nfb * S;
   for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < npieces;
        p += (size_t)gridDim.x * blockDim.x) {
@@ -70,10 +81,11 @@ __global__ void pack_bf16_kernel(const bf16_t* w0, const bf16_t* w1, const bf16_
     const int w = (int)((p >> 6) & 7), lane = (int)(p & 63);
     const int j = (int)(blk / G), g = (int)(blk % G);
     const int x = g % nfb, y = g / nfb;
-    const int row = (x * 8 + w) * 16 + (lane & 15);
+    const int prow = (x * 8 + w) * 16 + (lane & 15);
     const int k = (y * steps + j) * 32 + (lane >> 4) * 8;
     bf16x8 v = {};
-    if (row < N && k < K) {
+    if (prow < N && k < K) {
+      const int row = pack_row(prow, r0, il);
       const bf16_t* src;
       if (row < r0)
         src = w0 + (size_t)row * K;
@@ -89,11 +101,12 @@ __global__ void pack_bf16_kernel(const bf16_t* w0, const bf16_t* w1, const bf16_
 
 // float32 models keep row-major weights: the segments are concatenated.
 __global__ void pack_f32_kernel(const float* w0, const float* w1, const float* w2, int r0, int r1, int N, int K,
-                                float* dst) {
+                                bool il, float* dst) {
   const size_t n = (size_t)N * K;
   for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < n; p += (size_t)gridDim.x * blockDim.x) {
-    const int row = (int)(p / K);
-    const size_t c = p - (size_t)row * K;
+    const int prow = (int)(p / K);
+    const size_t c = p - (size_t)prow * K;
+    const int row = pack_row(prow, r0, il);
     const float* src = row < r0 ? w0 + (size_t)row * K
                                 : (row < r0 + r1 ? w1 + (size_t)(row - r0) * K : w2 + (size_t)(row - r0 - r1) * K);
     dst[p] = src[c];
@@ -231,7 +244,12 @@ struct BigGrid {
 // partials are added in split order in a second register set, which is
 // exactly what a consumer does with one slot per split: the single slot then
 // holds the decode kernel's bits (batch-invariant outputs in one slot).
-template <int MT, int NCH, int D, int FPW, int WAVES, bool CHAIN>
+//
+// SWIGLU (gate/up projection, one slot): the packed features interleave gate
+// and up fragments, so fragments 2j and 2j + 1 of a wave hold matching gate
+// and up sums in the same lanes; the epilogue writes bf16(silu(g) * u) with
+// the SwiGLU kernel's arithmetic instead of the float32 sums.
+template <int MT, int NCH, int D, int FPW, int WAVES, bool CHAIN, bool SWIGLU = false>
 __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGrid bg) {
   constexpr int NT = WAVES * 64, NS = NCH * KSTEPS;
   constexpr int BPW = WAVES * FPW / 8;           // packed blocks per workgroup
@@ -335,6 +353,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGr
     for (int f = 0; f < FPW; ++f)
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[f][t] = tot[CHAIN ? f : 0][CHAIN ? t : 0] + acc[f][t];
+  }
+  if (SWIGLU) {
+    static_assert(FPW % 2 == 0, "gate/up fragment pairs");
+    const int ffn = a.N >> 1;
+#pragma unroll
+    for (int f = 0; f < FPW; f += 2) {
+      const int col = ((blkx * 8 + fg0 + f) >> 1) * 16 + 4 * (lane >> 4);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int m = m0 + t * 16 + (lane & 15);
+        if (m >= a.M || col >= ffn) continue;
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = acc[f][t][e] / (1.0f + expf(-acc[f][t][e])) * acc[f + 1][t][e];
+        Elem<bf16_t>::store4(a.H, (size_t)m * ffn + col, o);
+      }
+    }
+    return;
   }
   // D layout: lane l holds D[4*(l/16) + r][l%16] = Y[m0 + 16t + l%16][n + 4*(l/16) + r]
   float* out = a.P + (size_t)yg * a.slot_stride;
@@ -451,7 +487,8 @@ size_t gemm_packed_bytes(const GemmPlan& p, int N, int K, int dtype) {
 }
 
 hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, const GemmPlan& p, void* dst,
-                       hipStream_t st) {
+                       bool interleave, hipStream_t st) {
+  if (interleave && (nseg != 2 || segs[0].rows != segs[1].rows || segs[0].rows % 16)) return hipErrorInvalidValue;
   const void* w0 = segs[0].ptr;
   const void* w1 = nseg > 1 ? segs[1].ptr : nullptr;
   const void* w2 = nseg > 2 ? segs[2].ptr : nullptr;
@@ -461,10 +498,10 @@ hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, cons
     const size_t npieces = gemm_packed_bytes(p, N, K, dtype) / 16;
     hipLaunchKernelGGL(pack_bf16_kernel, dim3(2048), dim3(256), 0, st, static_cast<const bf16_t*>(w0),
                        static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w2), r0, r1, N, K,
-                       (N + GROUP - 1) / GROUP, p.S, p.Ks / 32, npieces, static_cast<bf16_t*>(dst));
+                       (N + GROUP - 1) / GROUP, p.S, p.Ks / 32, npieces, interleave, static_cast<bf16_t*>(dst));
   } else {
     hipLaunchKernelGGL(pack_f32_kernel, dim3(2048), dim3(256), 0, st, static_cast<const float*>(w0),
-                       static_cast<const float*>(w1), static_cast<const float*>(w2), r0, r1, N, K,
+                       static_cast<const float*>(w1), static_cast<const float*>(w2), r0, r1, N, K, interleave,
                        static_cast<float*>(dst));
   }
   return hipGetLastError();
@@ -507,13 +544,18 @@ static BigGrid big_grid(const GemmPlan& p, int M, int N, bool invariant) {
 }
 
 template <int NCH>
-void launch_wide(const GemmArgs& a, const BigGrid& g, bool chain, hipStream_t st) {
-  if (chain)
-    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, true>), dim3(a.ntiles),
-                       dim3(BIGM_WAVES * 64), 0, st, a, g);
+void launch_wide(const GemmArgs& a, const BigGrid& g, bool chain, bool swiglu, hipStream_t st) {
+  const dim3 grid(a.ntiles), block(BIGM_WAVES * 64);
+  if (chain && swiglu)
+    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, true, true>), grid, block, 0, st,
+                       a, g);
+  else if (chain)
+    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, true>), grid, block, 0, st, a, g);
+  else if (swiglu)
+    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, false, true>), grid, block, 0, st,
+                       a, g);
   else
-    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, false>), dim3(a.ntiles),
-                       dim3(BIGM_WAVES * 64), 0, st, a, g);
+    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, false>), grid, block, 0, st, a, g);
 }
 
 int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant) {
@@ -521,11 +563,17 @@ int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invar
   return gemm_use_big(M, N, K) ? big_grid(p, M, N, invariant).nyg : p.S;
 }
 
+bool gemm_swiglu_fused(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant) {
+  return dtype == TRI_BF16 && gemm_use_big(M, N, K) && big_grid(p, M, N, invariant).nyg == 1;
+}
+
 hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, int N, const GemmPlan& plan, float* P,
-                       size_t slot_stride, bool invariant, hipStream_t st) {
+                       size_t slot_stride, bool invariant, hipStream_t st, void* swiglu_out) {
   if (M <= 0) return hipSuccess;
+  if (swiglu_out && !gemm_swiglu_fused(dtype, plan, M, N, K, invariant)) return hipErrorInvalidValue;
   if (dtype == TRI_BF16) {
     GemmArgs a;
+    a.H = static_cast<bf16_t*>(swiglu_out);
     a.X = static_cast<const bf16_t*>(X);
     a.M = M;
     a.K = K;
@@ -548,15 +596,15 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
           nch = c;
           break;
         }
-      const bool chain = invariant && g.cs > 1;
+      const bool chain = invariant && g.cs > 1, sw = swiglu_out != nullptr;
       switch (nch) {
-        case 1: launch_wide<1>(a, g, chain, st); break;
-        case 2: launch_wide<2>(a, g, chain, st); break;
-        case 3: launch_wide<3>(a, g, chain, st); break;
-        case 4: launch_wide<4>(a, g, chain, st); break;
-        case 5: launch_wide<5>(a, g, chain, st); break;
-        case 6: launch_wide<6>(a, g, chain, st); break;
-        case 8: launch_wide<8>(a, g, chain, st); break;
+        case 1: launch_wide<1>(a, g, chain, sw, st); break;
+        case 2: launch_wide<2>(a, g, chain, sw, st); break;
+        case 3: launch_wide<3>(a, g, chain, sw, st); break;
+        case 4: launch_wide<4>(a, g, chain, sw, st); break;
+        case 5: launch_wide<5>(a, g, chain, sw, st); break;
+        case 6: launch_wide<6>(a, g, chain, sw, st); break;
+        case 8: launch_wide<8>(a, g, chain, sw, st); break;
         default: return hipErrorInvalidValue;
       }
       return hipGetLastError();

@@ -150,8 +150,10 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
   }
 }
 
-// h = silu(gate) * up with gate = slots of columns [0, ffn), up = [ffn, 2 ffn);
-// one thread per four consecutive columns of one row.
+// h = silu(gate) * up.  The gate/up projection's columns interleave in groups
+// of 16 (the weight packing's order): columns [32j, 32j+16) are gate
+// features [16j, 16j+16) and [32j+16, 32j+32) the matching up features.
+// One thread per four consecutive columns of h in one row.
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ P, int nslots, size_t stride,
                                                      int rows, int ffn, T* __restrict__ h) {
@@ -159,9 +161,9 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ P
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * q4) return;
   const int r = i / q4, c = (i - r * q4) * 4;
-  const size_t rb = (size_t)r * 2 * ffn;
-  const f32x4 gt = slot_sum4(P, nslots, stride, rb + c);
-  const f32x4 up = slot_sum4(P, nslots, stride, rb + ffn + c);
+  const size_t rb = (size_t)r * 2 * ffn + (size_t)(c >> 4) * 32 + (c & 15);
+  const f32x4 gt = slot_sum4(P, nslots, stride, rb);
+  const f32x4 up = slot_sum4(P, nslots, stride, rb + 16);
   f32x4 o;
 #pragma unroll
   for (int e = 0; e < 4; ++e) o[e] = gt[e] / (1.0f + expf(-gt[e])) * up[e];
@@ -423,7 +425,7 @@ hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, 
 hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t stride, int rows, int ffn, void* h,
                          hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (ffn % 4 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  if (ffn % 16 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(((size_t)rows * (ffn / 4) + 255) / 256));
   TRI_DISPATCH(dtype,
                hipLaunchKernelGGL(swiglu_kernel<float>, grid, dim3(256), 0, st, P, nslots, stride, rows,

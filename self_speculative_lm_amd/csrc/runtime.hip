@@ -160,6 +160,7 @@ struct tri_session {
   float* rope;
   float* x;
   void* ybuf;
+  void* ybuf2;  // the fused gate/up + SwiGLU writes here; the two swap roles
   void* qbuf;
   void* abuf;
   float* part;
@@ -189,7 +190,7 @@ struct tri_session {
 namespace {
 
 struct SessionLayout {
-  size_t k, v, rope, x, y, q, a, part, part2, attn, logits, vws, ints, conf, total;
+  size_t k, v, rope, x, y, y2, q, a, part, part2, attn, logits, vws, ints, conf, total;
   size_t part_floats, part2_floats, attn_bytes, nints;
   size_t o_meta0, o_meta1, o_out_tok, o_out_commit, o_status, o_accept, o_committed, o_kvlen, o_drafts, o_ars;
   int ctx, kv_split;
@@ -240,6 +241,7 @@ SessionLayout session_layout(const tri_model* m, int max_batch, int max_ctx, int
   S.rope = region((size_t)S.ctx * (d.head_dim / 2) * 2 * sizeof(float));
   S.x = region((size_t)max_rows * d.d_model * sizeof(float));
   S.y = region((size_t)max_rows * ywidth * m->esz);
+  S.y2 = region((size_t)max_rows * ywidth * m->esz);
   S.q = region((size_t)max_rows * qd * m->esz);
   S.a = region((size_t)max_rows * qd * m->esz);
   S.part = region(S.part_floats * sizeof(float));
@@ -411,8 +413,15 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
     HIPCHK(launch_resid_norm(dt, s->x, s->part, oslots, ostride, n, D, L.n2, d.rms_eps, s->ybuf, s->st));
     {
       const size_t stride = (size_t)n * 2 * d.d_ffn;
-      PROF(PROF_GU, launch_gemm(dt, s->ybuf, n, D, L.gu, 2 * d.d_ffn, m->p_gu, s->part, stride, inv, s->st));
-      HIPCHK(launch_swiglu(dt, s->part, gemm_out_slots(dt, m->p_gu, n, 2 * d.d_ffn, D, inv), stride, n, d.d_ffn, s->ybuf, s->st));
+      if (gemm_swiglu_fused(dt, m->p_gu, n, 2 * d.d_ffn, D, inv)) {
+        PROF(PROF_GU, launch_gemm(dt, s->ybuf, n, D, L.gu, 2 * d.d_ffn, m->p_gu, s->part, stride, inv, s->st,
+                                  s->ybuf2));
+        std::swap(s->ybuf, s->ybuf2);  // h is the down projection's input
+      } else {
+        PROF(PROF_GU, launch_gemm(dt, s->ybuf, n, D, L.gu, 2 * d.d_ffn, m->p_gu, s->part, stride, inv, s->st));
+        HIPCHK(launch_swiglu(dt, s->part, gemm_out_slots(dt, m->p_gu, n, 2 * d.d_ffn, D, inv), stride, n, d.d_ffn,
+                             s->ybuf, s->st));
+      }
     }
     {
       prev_stride = (size_t)n * D;
@@ -732,7 +741,7 @@ int validate_desc(const tri_model_desc& d) {
   if (d.n_q_heads % d.n_kv_heads) return fail(TRI_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
   if (d.head_dim % 2) return fail(TRI_EINVAL, "head_dim must be even");
   if (d.d_model > 8192 || d.d_model % 4) return fail(TRI_EINVAL, "d_model must be a multiple of 4, <= 8192");
-  if (d.d_ffn % 4) return fail(TRI_EINVAL, "d_ffn must be a multiple of 4");
+  if (d.d_ffn % 16) return fail(TRI_EINVAL, "d_ffn must be a multiple of 16");
   if (!(d.rms_eps > 0) || !(d.rope_base > 1)) return fail(TRI_EINVAL, "bad rms_eps/rope_base");
   if (d.dtype == TRI_BF16) {
     if (d.head_dim != 128) return fail(TRI_EINVAL, "bf16 models need head_dim == 128");
@@ -842,13 +851,13 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   for (int l = 0; l < d.n_layers; ++l) {
     const ModelLayout::L& L = ML.layers[l];
     WSeg qkv[3] = {{weights[w], qd}, {weights[w + 1], kd}, {weights[w + 2], kd}};
-    HIPCHK(launch_pack(dt, qkv, 3, qd + 2 * kd, d.d_model, P.qkv, base + L.qkv, st));
+    HIPCHK(launch_pack(dt, qkv, 3, qd + 2 * kd, d.d_model, P.qkv, base + L.qkv, false, st));
     WSeg o = {weights[w + 3], d.d_model};
-    HIPCHK(launch_pack(dt, &o, 1, d.d_model, qd, P.o, base + L.o, st));
+    HIPCHK(launch_pack(dt, &o, 1, d.d_model, qd, P.o, base + L.o, false, st));
     WSeg gu[2] = {{weights[w + 4], d.d_ffn}, {weights[w + 5], d.d_ffn}};
-    HIPCHK(launch_pack(dt, gu, 2, 2 * d.d_ffn, d.d_model, P.gu, base + L.gu, st));
+    HIPCHK(launch_pack(dt, gu, 2, 2 * d.d_ffn, d.d_model, P.gu, base + L.gu, true, st));
     WSeg dn = {weights[w + 6], d.d_model};
-    HIPCHK(launch_pack(dt, &dn, 1, d.d_model, d.d_ffn, P.down, base + L.down, st));
+    HIPCHK(launch_pack(dt, &dn, 1, d.d_model, d.d_ffn, P.down, base + L.down, false, st));
     HIPCHK(hipMemcpyAsync(base + L.n1, weights[w + 7], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(hipMemcpyAsync(base + L.n2, weights[w + 8], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
     w += 9;
@@ -856,14 +865,14 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   HIPCHK(hipMemcpyAsync(base + ML.final_norm, weights[w++], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
   {
     WSeg lm = {weights[w++], d.vocab};
-    HIPCHK(launch_pack(dt, &lm, 1, d.vocab, d.d_model, P.lm, base + ML.lm_head, st));
+    HIPCHK(launch_pack(dt, &lm, 1, d.vocab, d.d_model, P.lm, base + ML.lm_head, false, st));
   }
   if (d.lora_rank > 0)
     for (int l = 0; l < d.n_layers; ++l) {
       WSeg a = {weights[w++], d.lora_rank};
-      HIPCHK(launch_pack(dt, &a, 1, d.lora_rank, qd, P.la, base + ML.layers[l].la, st));
+      HIPCHK(launch_pack(dt, &a, 1, d.lora_rank, qd, P.la, base + ML.layers[l].la, false, st));
       WSeg b = {weights[w++], d.d_model};
-      HIPCHK(launch_pack(dt, &b, 1, d.d_model, d.lora_rank, P.lb, base + ML.layers[l].lb, st));
+      HIPCHK(launch_pack(dt, &b, 1, d.d_model, d.lora_rank, P.lb, base + ML.layers[l].lb, false, st));
     }
   HIPCHK(hipStreamSynchronize(st));
   tri_model* m = new tri_model();
@@ -934,6 +943,7 @@ int tri_session_create(const tri_model* m, int max_batch, int max_ctx, int max_r
   s->rope = reinterpret_cast<float*>(base + S.rope);
   s->x = reinterpret_cast<float*>(base + S.x);
   s->ybuf = base + S.y;
+  s->ybuf2 = base + S.y2;
   s->qbuf = base + S.q;
   s->abuf = base + S.a;
   s->part = reinterpret_cast<float*>(base + S.part);

@@ -97,15 +97,20 @@ GemmPlan gemm_plan(int N, int K, int dtype, bool unsplit = false);
 // launch (segments concatenated by rows).
 size_t gemm_packed_bytes(const GemmPlan& p, int N, int K, int dtype);
 hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, const GemmPlan& p, void* dst,
-                       hipStream_t st);
+                       bool interleave, hipStream_t st);
 // Y = X W^T with W packed by launch_pack.
 // Output slots a launch_gemm of M rows writes (the consumer adds them in slot
 // order): the plan's S on the decode kernel, fewer on the large-M kernel
 // unless `invariant`.  With `invariant` every row's outputs are bit-identical
 // whatever M is (one slot per K split on both kernels).
 int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant);
+// Whether the gate/up projection of M rows can apply SwiGLU in its epilogue
+// (large-M kernel, one slot): launch_gemm(..., swiglu_out = h) then writes
+// h = bf16(silu(gate) * up) [M][N/2] instead of float32 slots, bit-identical
+// to the slots followed by the SwiGLU kernel.
+bool gemm_swiglu_fused(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant);
 hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, int N, const GemmPlan& plan,
-                       float* P, size_t slot_stride, bool invariant, hipStream_t st);
+                       float* P, size_t slot_stride, bool invariant, hipStream_t st, void* swiglu_out = nullptr);
 
 struct AttnLaunch {
   const void* q;

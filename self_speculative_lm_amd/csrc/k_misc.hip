@@ -150,6 +150,56 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
   }
 }
 
+// The same for head_dim 128 with vector accesses: 16 lanes per head, each
+// lane four consecutive columns of both halves (float4 slot and table loads),
+// four heads per wave.  Same arithmetic per element as rope_kv_kernel.
+constexpr int ROPE128_HPW = 4;                    // heads per wave
+constexpr int ROPE128_HEADS = 4 * ROPE128_HPW;    // heads per 256-thread workgroup
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict__ P, int nslots, size_t stride,
+                                                         int hq, int hkv, const int32_t* row_seq,
+                                                         const int32_t* row_pos, const float* __restrict__ rope,
+                                                         T* __restrict__ qout, T* __restrict__ kc,
+                                                         T* __restrict__ vc, int ctx, size_t css) {
+  constexpr int hd = 128, half = 64;
+  const int r = blockIdx.x;
+  const int h = blockIdx.y * ROPE128_HEADS + (int)(threadIdx.x >> 4);
+  if (h >= hq + 2 * hkv) return;
+  const int c = 4 * (threadIdx.x & 15);
+  const int pos = row_pos[r], seq = row_seq[r];
+  const size_t rb = (size_t)r * (hq + 2 * hkv) * hd + (size_t)h * hd;
+  const f32x4 xa = slot_sum4(P, nslots, stride, rb + c);
+  const f32x4 xb = slot_sum4(P, nslots, stride, rb + c + half);
+  if (h < hq + hkv) {
+    const f32x4 t0 = *reinterpret_cast<const f32x4*>(rope + ((size_t)pos * half + c) * 2);
+    const f32x4 t1 = *reinterpret_cast<const f32x4*>(rope + ((size_t)pos * half + c) * 2 + 4);
+    const float cs[4] = {t0[0], t0[2], t1[0], t1[2]}, sn[4] = {t0[1], t0[3], t1[1], t1[3]};
+    f32x4 ra, rbv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ra[e] = xa[e] * cs[e] - xb[e] * sn[e];
+      rbv[e] = xb[e] * cs[e] + xa[e] * sn[e];
+    }
+    if (h < hq) {
+      const size_t o = ((size_t)r * hq + h) * hd + c;
+      Elem<T>::store4(qout, o, ra);
+      Elem<T>::store4(qout, o + half, rbv);
+    } else {
+      const size_t o = (size_t)seq * css + ((size_t)(h - hq) * ctx + pos) * hd + c;
+      Elem<T>::store4(kc, o, ra);
+      Elem<T>::store4(kc, o + half, rbv);
+    }
+  } else {
+    const int kh = h - hq - hkv;
+    const size_t o = (size_t)seq * css + (size_t)kh * hd * ctx + pos;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Elem<T>::store(vc, o + (size_t)(c + e) * ctx, xa[e]);
+      Elem<T>::store(vc, o + (size_t)(c + half + e) * ctx, xb[e]);
+    }
+  }
+}
+
 // h = silu(gate) * up.  The gate/up projection's columns interleave in groups
 // of 16 (the weight packing's order): columns [32j, 32j+16) are gate
 // features [16j, 16j+16) and [32j+16, 32j+32) the matching up features.
@@ -410,6 +460,17 @@ hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, 
                           void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  if (hd == 128) {
+    const dim3 grid128(rows, (hq + 2 * hkv + ROPE128_HEADS - 1) / ROPE128_HEADS);
+    TRI_DISPATCH(dtype,
+                 hipLaunchKernelGGL(rope_kv128_kernel<float>, grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
+                                    row_seq, row_pos, rope, static_cast<float*>(qout), static_cast<float*>(kc),
+                                    static_cast<float*>(vc), ctx, css),
+                 hipLaunchKernelGGL(rope_kv128_kernel<bf16_t>, grid128, dim3(256), 0, st, P, nslots, stride, hq,
+                                    hkv, row_seq, row_pos, rope, static_cast<bf16_t*>(qout),
+                                    static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, css));
+    return hipGetLastError();
+  }
   const dim3 grid(rows, (hq + 2 * hkv + ROPE_HEADS - 1) / ROPE_HEADS);
   TRI_DISPATCH(dtype,
                hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(64 * ROPE_HEADS), 0, st, P, nslots, stride,

@@ -129,3 +129,31 @@ def test_8b_shape_batched_diffusion_teacher_forced(batch, plen):
     outs, sess = run(model, tm.TRI_DIFFUSION, 32, prompts, 2, max_ctx, trace=True, tau=0.0)
     assert all(len(o) == 64 and all(0 <= t < S8.vocab for t in o) for o in outs)
     check_teacher_forced(S8, oms, sess, max_ctx, prompts)
+
+
+def test_8b_shape_mixed_batch_teacher_forced_and_equals_ar():
+    """Six sequences, AR and self-speculation in the same two forwards (up to
+    168 draft rows: the large-M GEMM): each sequence commits exactly its AR
+    continuation (rows are bit-identical whatever the batch), and every traced
+    forward matches the oracle."""
+    import self_speculative_lm_amd as tm
+    model, *oms = get(S8)
+    prompts = [seeded.prompt(64 + 5 * i, S8.vocab, stream=40 + i) for i in range(6)]
+    max_ctx = 64 + 5 * 6 + 3 * 33 + 64
+    AR, SS = tm.TRI_AR, tm.TRI_SELFSPEC
+    sched = [[SS, AR, SS, SS, AR, SS], [AR, SS, SS, AR, SS, SS]]
+    sess = tm.Session(model, max_batch=6, max_ctx=max_ctx, max_rows=6 * 34)
+    for i, p in enumerate(prompts):
+        sess.prefill(i, p)
+    sess.set_trace(True)
+    outs = [[] for _ in prompts]
+    for modes in sched:
+        toks, st = sess.decode_step_mixed(modes, 32)
+        for i, m in enumerate(modes):
+            got = [int(t) for t in toks[i] if t >= 0]
+            assert len(got) == (2 if m == AR else st[i][2] + 1)
+            outs[i] += got
+    for i, p in enumerate(prompts):
+        ar, _ = run(model, AR, 1, [p], len(outs[i]), max_ctx)
+        assert outs[i] == ar[0][: len(outs[i])], i
+    check_teacher_forced(S8, oms, sess, max_ctx, prompts)

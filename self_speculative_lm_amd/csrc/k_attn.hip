@@ -341,6 +341,10 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
 
   // 4. Merge the key groups into key group 0 (per lane and query: the lanes
   //    of one query share m_run, and l is reduced across them afterwards).
+  //    The two-term sums are written as explicit fmaf: left to contraction,
+  //    the compiler fused one product or the other depending on the
+  //    instantiation, and a query's last bit then depended on the launch
+  //    shape (two query tiles per wave differed in single elements).
   if constexpr (KW > 1) {
     constexpr int NC = 34;  // O^T fragment (32 floats), m, l
     static_assert((KW - 1) * QW * QT * NC * 64 * 4 <= (int)sizeof(ks), "merge area fits the K tiles");
@@ -371,8 +375,8 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[q][dt][r] = oacc[q][dt][r] * w1 + d[(dt * 4 + r) * 64] * w2;
-        l_run[q] = l_run[q] * w1 + l2 * w2;
+          for (int r = 0; r < 4; ++r) oacc[q][dt][r] = fmaf(d[(dt * 4 + r) * 64], w2, oacc[q][dt][r] * w1);
+        l_run[q] = fmaf(l2, w2, l_run[q] * w1);
         m_run[q] = M;
       }
     }
@@ -443,8 +447,8 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* part_o, 
       } else if (c0 + i < ns) {
         const float Mn = fmaxf(M, m[i]);
         const float wa = exp2f(M - Mn), wb = exp2f(m[i] - Mn);
-        L = L * wa + l[i] * wb;
-        O = O * wa + o[i] * wb;
+        L = fmaf(l[i], wb, L * wa);
+        O = fmaf(o[i], wb, O * wa);
         M = Mn;
       }
     }
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, const floa
     const float p = (key < hi) ? expf(s - m_new) : 0.f;
     float ps = p;
     for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
-    l = l * alpha + ps;
+    l = fmaf(l, alpha, ps);
     o0 *= alpha;
     o1 *= alpha;
     const int nk = min(64, hi - j0);
@@ -510,6 +514,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, const floa
 // query tiles per kv head (each K/V tile read once per 128 query vectors).
 // The rounding depends on neither choice.
 static void attn_shape(int qtiles, int max_hi, int* qw, int* qt) {
+  if (qtiles >= 64) {  // prefill-sized blocks (>= 256 rows of one sequence)
+    *qw = 4;
+    *qt = max_hi > 1024 ? 2 : 1;
+    return;
+  }
   *qt = (qtiles > 8 && max_hi > 4096) ? 2 : 1;
   *qw = (*qt == 1 && (qtiles <= 2 || max_hi <= 1536)) ? 2 : 4;
 }

@@ -129,8 +129,8 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
       const float xb = slot_sum(P, nslots, stride, rb + c + half);
       const float cs = rope[((size_t)pos * half + c) * 2];
       const float sn = rope[((size_t)pos * half + c) * 2 + 1];
-      const float ra = xa * cs - xb * sn;
-      const float rbv = xb * cs + xa * sn;
+      const float ra = fmaf(xa, cs, -(xb * sn));
+      const float rbv = fmaf(xb, cs, xa * sn);
       if (h < hq) {
         const size_t o = ((size_t)r * hq + h) * hd + c;
         Elem<T>::store(qout, o, ra);
@@ -177,8 +177,8 @@ __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict
     f32x4 ra, rbv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ra[e] = xa[e] * cs[e] - xb[e] * sn[e];
-      rbv[e] = xb[e] * cs[e] + xa[e] * sn[e];
+      ra[e] = fmaf(xa[e], cs[e], -(xb[e] * sn[e]));
+      rbv[e] = fmaf(xb[e], cs[e], xa[e] * sn[e]);
     }
     if (h < hq) {
       const size_t o = ((size_t)r * hq + h) * hd + c;

@@ -18,14 +18,15 @@ computes, written from the public write-ups of Nemotron-Labs-Diffusion:
 * [Abstract] the arXiv abstract page (aihot.42aifuture), arXiv:2607.05722.
 
 Where the pages leave a step open, the reading taken is named in the function
-that takes it (R1..R19 in the design notes use the same numbering).
+that takes it (R1..R20 in the design notes use the same numbering).
 
 Pins (tests run with ``-m "not gpu"``) tie every function here to something
 other than itself: brute-force masked attention, an independent torch-CPU
 textbook forward, RoPE closed forms, a brute-force acceptance loop, the
 losslessness of self-speculation against greedy AR (also in mixed AR /
 self-speculation steps), KV-rollback equality with an AR cache, the diffusion
-threshold edge cases, and closed forms of the mode choice by concurrency.  No function here is
+threshold edge cases, closed forms of the mode choice by concurrency, and
+closed forms plus a textbook replay of the speed-of-light analysis.  No function here is
 "parity unpinned" except the diffusion trajectory itself for thresholds
 strictly inside (0, 1), for which the pages print no worked example.
 """
@@ -34,3 +35,4 @@ from .model import OracleModel, Row, KVCache, forward  # noqa: F401
 from .sampler import vocab_reduce, commit_set, accept_length  # noqa: F401
 from .decode import OracleSession, MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC  # noqa: F401
 from .policy import choose_modes, forward_ms, step_rate  # noqa: F401
+from .sol import sol_block  # noqa: F401

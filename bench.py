@@ -291,6 +291,48 @@ def concurrency_sweep(args):
                       "ms": [round(t, 3) for t in grid_ms]}), flush=True)
 
 
+def sol_analysis(args):
+    """Speed-of-light analysis (tri_sol_block) on the 8B-class decoder at block
+    `--block`, for 1 and 8 sequences: per call, the serial pass (block
+    forwards) and the parallel pass over the same block.  With seeded random
+    weights the forward counts exercise the tool; they are not the trained
+    model's headroom."""
+    import numpy as np
+    import torch
+    import seeded
+    import self_speculative_lm_amd as tm
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    shape = seeded.MODEL_8B
+    k = args.block
+    n_blocks = 4
+    model = build_model(shape, dev)
+    for n in (1, 8):
+        max_ctx = args.prompt + (n_blocks + 1) * k + 64
+        sess = tm.Session(model, max_batch=n, max_ctx=max_ctx, max_rows=max(args.max_rows, n * (2 * k + 1)),
+                          device=dev)
+        for i in range(n):
+            sess.prefill(i, seeded.prompt(args.prompt, shape.vocab, stream=200 + i))
+        sess.sol_block(k)                                    # warm-up block
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = [sess.sol_block(k) for _ in range(n_blocks)]
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        fw = np.array([r["forwards"] for r in res], dtype=np.float64)   # [blocks][n]
+        par = int(fw.max(axis=1).sum())                                 # batched parallel forwards run
+        forwards = n_blocks * k + par
+        print(json.dumps({
+            "metric": "speed-of-light analysis, 8B-class, random-init weights", "batch": n, "block": k,
+            "blocks": n_blocks, "serial_forwards_per_block": k,
+            "sol_forwards_per_block": round(float(fw.mean()), 3),
+            "sol_tokens_per_forward": round(float((k / fw).mean()), 3),
+            "ms_per_block_analysis": round(dt * 1e3 / n_blocks, 2),
+            "ms_per_forward": round(dt * 1e3 / forwards, 3)}), flush=True)
+        sess.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,18 +348,23 @@ def main():
                     help="time block_causal_attn alone at the attention-only shapes instead of the decode round")
     ap.add_argument("--concurrency", action="store_true",
                     help="mixed AR / self-speculation steps at 1..64 sequences with the mode choice by concurrency")
+    ap.add_argument("--sol", action="store_true",
+                    help="speed-of-light analysis (serial denoising + parallel pass) at 1 and 8 sequences")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the decode step is built and measured on a single "
-              "MI355X (no multi-GPU path in this build).", file=sys.stderr)
+              "MI355X (there is no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     if args.attn:
         attention_alone(args)
         return
     if args.concurrency:
         concurrency_sweep(args)
+        return
+    if args.sol:
+        sol_analysis(args)
         return
 
     import numpy as np

@@ -161,6 +161,30 @@ int tri_decode_step(tri_session* session, int mode, int block, float threshold,
 int tri_decode_step_mixed(tri_session* session, const int32_t* modes, int block,
                           int32_t* out_tokens, tri_seq_stats* out_stats);
 
+/* Speed-of-light analysis of the next block of every prefilled sequence
+ * [Notes §7; Abstract]: how few forwards an ideal sampler would need to reach
+ * the block that serial denoising converges to.
+ *   1. Serial denoising: the diffusion block at threshold 1, one commit per
+ *      forward (the most confident masked position, lowest on ties).  It
+ *      fixes the target block and the serial order of its positions.
+ *   2. Parallel pass from the same state: each forward commits every masked
+ *      position whose greedy token already equals its target; when none does,
+ *      the next position of the serial order.  Every forward commits >= 1.
+ * The sequences end as after the serial block (as tri_decode_step in
+ * TRI_DIFFUSION mode at threshold 1 leaves them), so calls chain over a
+ * generation.  block in [1, 64].  Host outputs, [max_batch][block] and
+ * [max_batch], -1 for sequences not prefilled:
+ *   out_target   the target tokens;
+ *   out_order    out_order[j] = the position committed by serial forward j;
+ *   out_step     the parallel forward (0-based) at which each position commits;
+ *   out_forwards the parallel pass's forward count (block / it = SOL tokens
+ *                per forward; the serial pass always takes block forwards).
+ * Errors: TRI_ESTATE (no prefilled sequence, no pending token), TRI_ECAPACITY
+ * (L + block > max_ctx, or more than max_rows rows), TRI_ENUMERIC (non-finite
+ * logits; the sequences are then left as before the call).  Synchronous. */
+int tri_sol_block(tri_session* session, int block, int32_t* out_target, int32_t* out_order,
+                  int32_t* out_step, int32_t* out_forwards);
+
 /* Mode choice by concurrency for one mixed step (host only, no device work).
  * Chooses per sequence TRI_AR or TRI_SELFSPEC to maximise the step's expected
  * committed tokens per millisecond:

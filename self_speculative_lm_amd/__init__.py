@@ -143,6 +143,17 @@ class Session:
         check(lib().tri_decode_step_mixed(self.handle, _ip(m), block, _ip(out), st))
         return out, [(s.n_committed, s.n_forwards, s.accept_len, s.n_flags) for s in st]
 
+    def sol_block(self, block: int = 32):
+        """Speed-of-light analysis of every prefilled sequence's next block;
+        the sequences advance by the serial block.  Returns a dict of arrays
+        target, order, step ([max_batch][block]) and forwards ([max_batch]),
+        -1 for sequences not prefilled."""
+        tgt = np.full((self.max_batch, block), -1, dtype=np.int32)
+        order, step = tgt.copy(), tgt.copy()
+        fw = np.full(self.max_batch, -1, dtype=np.int32)
+        check(lib().tri_sol_block(self.handle, block, _ip(tgt), _ip(order), _ip(step), _ip(fw)))
+        return {"target": tgt, "order": order, "step": step, "forwards": fw}
+
     def set_lora(self, enabled: bool) -> None:
         check(lib().tri_set_lora(self.handle, int(bool(enabled))))
 

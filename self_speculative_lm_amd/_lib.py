@@ -50,6 +50,7 @@ SIGNATURES = {
     "tri_prefill": (I, [P, I, IP, I]),
     "tri_decode_step": (I, [P, I, I, F, IP, ctypes.POINTER(SeqStats)]),
     "tri_decode_step_mixed": (I, [P, IP, I, IP, ctypes.POINTER(SeqStats)]),
+    "tri_sol_block": (I, [P, I, IP, IP, IP, IP]),
     "tri_choose_modes": (I, [IP, ctypes.POINTER(ctypes.c_double), I, I, ctypes.POINTER(ctypes.c_double), IP, I, IP]),
     "tri_set_lora": (I, [P, I]),
     "kv_append": (I, [P, I, I]),

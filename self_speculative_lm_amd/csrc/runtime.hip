@@ -511,8 +511,9 @@ int step_ar(tri_session* s, const std::vector<int>& act, int stride, int32_t* ou
   return TRI_OK;
 }
 
+// order (optional): the positions of each block in the order they were committed.
 int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau, int stride, int32_t* out_tokens,
-                   tri_seq_stats* st) {
+                   tri_seq_stats* st, std::vector<std::vector<int>>* order = nullptr) {
   const int mask = s->m->d.vocab;
   const size_t na = act.size();
   std::vector<std::vector<int32_t>> y(na, std::vector<int32_t>(B, mask));
@@ -554,6 +555,7 @@ int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau
         y[j][i] = s->hints[s->o_out_tok + r];
         done[j][i] = 1;
         --remaining[j];
+        if (order) (*order)[j].push_back(i);
         if (std::fabs(s->hconf[r] - tau) < 1e-6f) ++flags[j];
       }
     }
@@ -567,6 +569,67 @@ int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau
     S.tokens.insert(S.tokens.end(), y[j].begin(), y[j].end());
     for (int i = 0; i < B; ++i) out_tokens[(size_t)act[j] * stride + i] = y[j][i];
     if (st) st[act[j]] = tri_seq_stats{B, fwd[j], -1, flags[j]};
+  }
+  return TRI_OK;
+}
+
+// The parallel pass of the speed-of-light analysis [Notes §7]: from the state
+// before the block, every forward commits each masked position whose greedy
+// token already equals its target, or, when none does, the next position of
+// the serial order.  The sampler still computes every row's greedy token on
+// the device; only the comparison with the target runs here.  step[j][i] gets
+// the forward at which position i of act[j] was committed, fwd[j] the count.
+int sol_parallel(tri_session* s, const std::vector<int>& act, int B, const std::vector<std::vector<int32_t>>& target,
+                 const std::vector<std::vector<int>>& order, std::vector<std::vector<int>>& step,
+                 std::vector<int>& fwd) {
+  const int mask = s->m->d.vocab;
+  const size_t na = act.size();
+  std::vector<std::vector<int32_t>> y(na, std::vector<int32_t>(B, mask));
+  std::vector<int> remaining(na, B), next(na, 0);
+  step.assign(na, std::vector<int>(B, -1));
+  fwd.assign(na, 0);
+  bool first = true;
+  for (;;) {
+    HostRows R;
+    std::vector<int> blk_row(na, -1);
+    for (size_t j = 0; j < na; ++j) {
+      if (remaining[j] == 0) continue;
+      const Seq& S = s->seqs[act[j]];
+      const int L = (int)S.tokens.size();
+      if (first) pending_rows(S, act[j], R, 0);
+      R.block_start.push_back(R.n());
+      blk_row[j] = R.n();
+      for (int i = 0; i < B; ++i) R.add(y[j][i], L + i, L + B, act[j], 0, y[j][i] == mask ? 2 : 3);
+      R.close_slot(act[j]);
+    }
+    if (R.n() == 0) break;
+    R.block_start.push_back(R.n());
+    int rc = stage_meta(s, 0, R, {}, {});
+    if (!rc) rc = upload_meta(s, 0);
+    if (!rc) rc = forward(s, 0, R, s->logits);
+    if (!rc) rc = sample(s, 0, R, s->logits, 1.f, 0);
+    if (!rc) rc = d2h_ints(s, s->o_out_tok, R.n());
+    if (!rc) rc = d2h_ints(s, s->o_status, 1);
+    if (rc) return rc;
+    HIPCHK(hipStreamSynchronize(s->st));
+    if (s->hints[s->o_status]) return fail(TRI_ENUMERIC, "non-finite logits in the speed-of-light pass");
+    for (size_t j = 0; j < na; ++j) {
+      if (blk_row[j] < 0) continue;
+      std::vector<int> now;
+      for (int i = 0; i < B; ++i)
+        if (y[j][i] == mask && s->hints[s->o_out_tok + blk_row[j] + i] == target[j][i]) now.push_back(i);
+      if (now.empty()) {
+        while (y[j][order[j][next[j]]] != mask) ++next[j];
+        now.push_back(order[j][next[j]]);
+      }
+      for (int i : now) {
+        y[j][i] = target[j][i];
+        step[j][i] = fwd[j];
+      }
+      remaining[j] -= (int)now.size();
+      ++fwd[j];
+    }
+    first = false;
   }
   return TRI_OK;
 }
@@ -1126,6 +1189,72 @@ int tri_decode_step_mixed(tri_session* s, const int32_t* modes, int block, int32
     for (int b = 0; b < s->max_batch; ++b) out_stats[b] = tri_seq_stats{0, 0, -1, 0};
   s->ev_used = s->prof_class >= 0 ? s->ev_used : 0;
   return step_round(s, act, spec, block, stride, out_tokens, out_stats);
+}
+
+int tri_sol_block(tri_session* s, int block, int32_t* out_target, int32_t* out_order, int32_t* out_step,
+                  int32_t* out_forwards) {
+  if (!s || !out_target || !out_order || !out_step || !out_forwards) return fail(TRI_EINVAL, "null argument");
+  if (block < 1 || block > 64) return fail(TRI_EINVAL, "block %d outside [1, 64]", block);
+  std::vector<int> act;
+  int rows = 0;
+  for (int b = 0; b < s->max_batch; ++b) {
+    const Seq& S = s->seqs[b];
+    if (!S.active) continue;
+    const int L = (int)S.tokens.size();
+    const int pend = L - S.kv_len;
+    if (pend < 1) return fail(TRI_ESTATE, "sequence %d has no pending token (kv_len %d, L %d)", b, S.kv_len, L);
+    if (L + block > s->max_ctx) return fail(TRI_ECAPACITY, "sequence %d would pass max_ctx %d", b, s->max_ctx);
+    rows += pend + block;
+    act.push_back(b);
+  }
+  if (act.empty()) return fail(TRI_ESTATE, "no prefilled sequence");
+  if (rows > s->max_rows) return fail(TRI_ECAPACITY, "step needs %d rows, session allows %d", rows, s->max_rows);
+  const size_t na = act.size(), cells = (size_t)s->max_batch * block;
+  for (size_t i = 0; i < cells; ++i) out_target[i] = out_order[i] = out_step[i] = -1;
+  for (int b = 0; b < s->max_batch; ++b) out_forwards[b] = -1;
+  s->ev_used = s->prof_class >= 0 ? s->ev_used : 0;
+  struct Saved {
+    size_t L;
+    int kv_len, written_hi;
+  };
+  std::vector<Saved> saved(na);
+  for (size_t j = 0; j < na; ++j) {
+    const Seq& S = s->seqs[act[j]];
+    saved[j] = Saved{S.tokens.size(), S.kv_len, S.written_hi};
+  }
+  // serial denoising: the diffusion block at threshold 1 commits exactly one
+  // position per forward (no confidence exceeds 1)
+  std::vector<int32_t> toks(cells + (size_t)s->max_batch, -1);
+  std::vector<std::vector<int>> order(na);
+  int rc = step_diffusion(s, act, block, 1.f, block, toks.data(), nullptr, &order);
+  if (rc) return rc;
+  std::vector<std::vector<int32_t>> target(na);
+  for (size_t j = 0; j < na; ++j) {
+    Seq& S = s->seqs[act[j]];
+    target[j].assign(S.tokens.end() - block, S.tokens.end());
+    S.tokens.resize(saved[j].L);
+    S.kv_len = saved[j].kv_len;
+    S.written_hi = saved[j].written_hi;
+  }
+  std::vector<std::vector<int>> step;
+  std::vector<int> fwd;
+  rc = sol_parallel(s, act, block, target, order, step, fwd);
+  if (rc) return rc;  // the sequences stay as before the call
+  for (size_t j = 0; j < na; ++j) {
+    Seq& S = s->seqs[act[j]];
+    const int L = (int)saved[j].L;
+    S.kv_len = L;  // as after the serial block
+    S.written_hi = L;
+    S.tokens.insert(S.tokens.end(), target[j].begin(), target[j].end());
+    const size_t o = (size_t)act[j] * block;
+    for (int i = 0; i < block; ++i) {
+      out_target[o + i] = target[j][i];
+      out_order[o + i] = order[j][i];
+      out_step[o + i] = step[j][i];
+    }
+    out_forwards[act[j]] = fwd[j];
+  }
+  return TRI_OK;
 }
 
 int tri_choose_modes(const int32_t* grid_rows, const double* grid_ms, int n_grid, int n_seq, const double* expected,

@@ -128,6 +128,41 @@ class OracleSession:
         self.rounds += 1
         return y
 
+    def diffusion_block_scheduled(self, block: int, counts: List[int]) -> List[int]:
+        """A diffusion block whose t-th forward commits the min(counts[t mod
+        len(counts)], remaining) most confident masked positions (lowest
+        position on ties), each with its greedy token.  A controlled stand-in
+        for a trained sampler's commit rate (the pages report about 2.6x TPF
+        for diffusion mode, [Blog] performance highlights): the forwards are
+        those of the threshold rule, only the number committed is fixed."""
+        if not counts or min(counts) < 1:
+            raise ValueError("commit counts must be >= 1")
+        mask = self.model.shape.mask_id
+        L = self.L
+        y = [mask] * block
+        done = [False] * block
+        first, t = True, 0
+        while not all(done):
+            clean = self.clean_rows() if first else []
+            rows = clean + [Row(y[i], L + i, L + block) for i in range(block)]
+            logits = self.run(rows)
+            if first:
+                self.kv_append(len(clean))
+                first = False
+            cand = []
+            for i in range(block):
+                if not done[i]:
+                    tok, conf = vocab_reduce(logits[len(clean) + i])
+                    cand.append((-conf, i, tok))
+            cand.sort()
+            for _, i, tok in cand[: counts[t % len(counts)]]:
+                y[i] = tok
+                done[i] = True
+            t += 1
+        self.tokens.extend(y)
+        self.rounds += 1
+        return y
+
     def draft(self, k: int, lora: bool = False):
         """The draft forward: returns (g0, drafts) and appends the pending rows."""
         mask = self.model.shape.mask_id

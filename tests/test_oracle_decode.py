@@ -203,3 +203,57 @@ def test_tpf_definition_matches_published_ratio():
     tpf = len(out) / s.forwards
     tpr = len(out) / len(s.accepts)
     assert tpr == pytest.approx(g["forwards_per_round"] * tpf)
+
+
+# ------------------------------------------------ scheduled commit counts
+def test_scheduled_diffusion_reduces_to_the_threshold_edge_cases():
+    shape = seeded.TINY_SHARP
+    for stream in range(3):
+        p = seeded.prompt(14, shape.vocab, stream=stream)
+        a, b = OracleSession(model(shape), 96), OracleSession(model(shape), 96)
+        a.prefill(p)
+        b.prefill(p)
+        assert a.diffusion_block_scheduled(8, [1]) == b.diffusion_block(8, 1.0)   # one per forward
+        assert a.forwards == b.forwards == 8 and a.tokens == b.tokens
+        c, d = OracleSession(model(shape), 96), OracleSession(model(shape), 96)
+        c.prefill(p)
+        d.prefill(p)
+        assert c.diffusion_block_scheduled(8, [8]) == d.diffusion_block(8, 0.0)   # the whole block at once
+        assert c.forwards == d.forwards == 1
+
+
+def test_scheduled_diffusion_commits_the_most_confident_counts():
+    shape = seeded.TINY_SHARP
+    rng = np.random.default_rng(4)
+    for trial in range(4):
+        counts = [int(c) for c in rng.integers(1, 5, size=int(rng.integers(1, 4)))]
+        s = session(shape, prompt_len=12)
+        s.keep_logits = True
+        n0 = len(s.records)
+        L = s.L
+        y = s.diffusion_block_scheduled(10, counts)
+        recs = s.records[n0:]
+        done = set()
+        for t, rec in enumerate(recs):
+            block = rec.logits[-10:]
+            masked = [i for i in range(10) if i not in done]
+            confs = sorted(masked, key=lambda i: (-vocab_reduce(block[i])[1], i))
+            now = confs[: counts[t % len(counts)]]
+            for i in now:
+                assert y[i] == vocab_reduce(block[i])[0]
+                assert rec.rows[-10 + i].token == shape.mask_id
+            done.update(now)
+        assert len(done) == 10 and s.L == L + 10
+        # forwards: the fewest t with sum of the cycled counts >= 10
+        need, t = 10, 0
+        while need > 0:
+            need -= counts[t % len(counts)]
+            t += 1
+        assert len(recs) == t
+
+
+def test_scheduled_diffusion_rejects_bad_counts():
+    s = session(seeded.TINY)
+    for bad in ([], [0], [2, -1]):
+        with pytest.raises(ValueError):
+            s.diffusion_block_scheduled(8, bad)

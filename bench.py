@@ -168,6 +168,51 @@ def attention_alone(args):
             torch.cuda.empty_cache()
 
 
+def attention_split_sweep(args):
+    """Block-causal attention alone at prefixes 4K..32K, batch 1 and 8, with the
+    key split forced to each power of two in [256, 4096] and the library's own
+    pick (0): one JSON line per (prefix, batch), microseconds per launch (HIP
+    events around 30 back-to-back calls).  The data behind the split cost model."""
+    import torch
+    import self_speculative_lm_amd as tm
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    hq, hkv, hd, nb = 32, 8, 128, 32
+    g = torch.Generator(device=dev).manual_seed(3)
+    for P in (4096, 8192, 16384, 32768):
+        for b in (1, 8):
+            L = P + nb
+            ctx = (L + 63) // 64 * 64
+            kc = torch.randn((b, hkv, ctx, hd), generator=g, device=dev).to(torch.bfloat16)
+            vc = torch.randn((b, hkv, hd, ctx), generator=g, device=dev).to(torch.bfloat16)
+            q = torch.randn((b * nb, hq, hd), generator=g, device=dev).to(torch.bfloat16)
+            out = torch.empty_like(q)
+            ss = torch.arange(0, b * nb + 1, nb, dtype=torch.int32, device=dev)
+            hi = torch.full((b * nb,), L, dtype=torch.int32, device=dev)
+            res = {}
+            for sp in (0, 256, 512, 1024, 2048, 4096):
+                ws = torch.empty(tm.block_causal_attn_ws_bytes(b * nb, hq, hd, L, sp), dtype=torch.uint8, device=dev)
+
+                def run():
+                    tm.block_causal_attn(q, kc, vc, ss, hi, out, 1.0 / math.sqrt(hd), max_rows_per_seq=nb,
+                                         max_hi=L, kv_split=sp, ws=ws)
+                for _ in range(3):
+                    run()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(30):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+                res[sp] = round(e0.elapsed_time(e1) * 1e3 / 30, 2)
+                del ws
+            print(json.dumps({"metric": "block-causal attention alone, us by key split", "prefix": P, "batch": b,
+                              "us_by_split": res}), flush=True)
+            del kc, vc, q, out
+            torch.cuda.empty_cache()
+
+
 def build_model(shape, dev):
     import torch
     import self_speculative_lm_amd as tm
@@ -333,6 +378,144 @@ def sol_analysis(args):
         sess.close()
 
 
+def diffusion_sweep(args):
+    """The 8B-class decoder in diffusion mode: 32-token blocks from a 1024-token
+    prompt, 512 new tokens per sequence, thresholds 0.5 / 0.7 / 0.9 at 1, 4 and
+    16 concurrent sequences, then AR at 16 sequences for comparison.  With
+    random-init weights no confidence passes a threshold, so every forward
+    commits the single forced position; a labelled controlled run replays a
+    seeded commit schedule of 2.6 positions per forward on average (the pages'
+    2.6x diffusion TPF) with every forward still run in full."""
+    import numpy as np
+    import torch
+    import seeded
+    import self_speculative_lm_amd as tm
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    shape = seeded.MODEL_8B
+    B, plen, n_new = 32, 1024, 512
+    model = build_model(shape, dev)
+    rng = np.random.default_rng(5)
+    sched = [int(c) for c in np.where(rng.random(64) < 0.6, 3, 2)]
+    qd = shape.n_q_heads * shape.head_dim
+
+    def fwd_flops(n, L):
+        # projections + lm_head per row, attention over L + B keys per block row
+        rows = n * B
+        return step_flops(shape, rows) + shape.n_layers * 4.0 * qd * rows * (L + B)
+
+    def run(n, mode, tau=0.0, controlled=False):
+        max_ctx = plen + n_new + 2 * B + 64
+        # a block's first forward carries the previous block's 32 pending rows
+        sess = tm.Session(model, max_batch=n, max_ctx=max_ctx, max_rows=max(args.max_rows, n * (2 * B + 1)),
+                          device=dev)
+        for i in range(n):
+            sess.prefill(i, seeded.prompt(plen, shape.vocab, stream=300 + i))
+            if controlled:
+                sess.set_commit_schedule(i, sched)
+        step_b = 1 if mode == tm.TRI_AR else B
+        sess.decode_step(mode, step_b, tau)                 # warm-up step (not timed)
+        torch.cuda.synchronize()
+        committed = forwards = 0
+        bytes_, flops = 0.0, 0.0
+        t0 = time.perf_counter()
+        while committed < n * n_new:
+            L = len(sess.state(0)[0])
+            fb = sess.forward_bytes(step_b)
+            _, st = sess.decode_step(mode, step_b, tau)
+            f = max(x[1] for x in st[:n])
+            committed += sum(x[0] for x in st[:n])
+            forwards += f
+            bytes_ += fb * f
+            flops += fwd_flops(n, L) * f if mode != tm.TRI_AR else step_flops(shape, n) * f
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        sess.close()
+        gbs, tfs = bytes_ / dt / 1e9, flops / dt / 1e12
+        bound = "mfma" if (mode != tm.TRI_AR and n >= 16) else "hbm"
+        return {"tok_s": round(committed / dt, 1), "tok_s_per_seq": round(committed / dt / n, 1),
+                "tpf": round(committed / n / forwards, 3), "forwards": forwards,
+                "ms_per_forward": round(dt * 1e3 / forwards, 3),
+                "roofline": {"bound": bound,
+                             "achieved": round(tfs if bound == "mfma" else gbs, 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS,
+                             "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                             "frac": round((tfs / MFMA_BF16_PEAK_TFLOPS) if bound == "mfma" else (gbs / HBM_PEAK_GBS), 4)}}
+
+    base = {"metric": "8B-class diffusion mode, block 32, 1024-token prompt, 512 new tokens per sequence",
+            "data": "synthetic (seeded random-init weights, uniform random prompts)"}
+    for n in (1, 4, 16):
+        for tau in (0.5, 0.7, 0.9):
+            res = dict(base, batch=n, threshold=tau, **run(n, tm.TRI_DIFFUSION, tau))
+            print(json.dumps(res), flush=True)
+        res = dict(base, batch=n, threshold="controlled commit schedule, mean 2.6 per forward",
+                   **run(n, tm.TRI_DIFFUSION, 0.9, controlled=True))
+        print(json.dumps(res), flush=True)
+    res = dict(base, metric="8B-class AR mode, 1024-token prompt, 512 new tokens per sequence", batch=16,
+               **run(16, tm.TRI_AR))
+    print(json.dumps(res), flush=True)
+
+
+def long_prefix_14b(args):
+    """The 14B-class decoder in self-speculation at batch 1 behind a 16384-token
+    random prefix, draft block 32, with the rank-128 o_proj LoRA on the draft
+    rows, 256 new tokens: committed tokens/s and the per-forward HBM fraction
+    (weights + KV + LoRA of the draft forward)."""
+    import torch
+    import seeded
+    import self_speculative_lm_amd as tm
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    shape = seeded.MODEL_14B
+    k, plen, n_new = args.block, 16384, 256
+    t0 = time.time()
+    log(f"generating and uploading {shape.n_params() / 1e9:.2f}B seeded weights")
+    tensors = upload_weights(shape, dev)
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f}s")
+    model = tm.Model(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn,
+                     shape.vocab, tensors, dtype=tm.TRI_BF16, lora_rank=shape.lora_rank)
+    del tensors
+    torch.cuda.empty_cache()
+    max_ctx = plen + n_new + 2 * (k + 1) + 64
+    sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=args.max_rows, device=dev)
+    sess.set_lora(True)
+    prompt = seeded.prompt(plen, shape.vocab, stream=400)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sess.prefill(0, prompt)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t1
+    log(f"prefill of {plen} tokens: {prefill_s:.2f} s")
+    sess.decode_step(tm.TRI_SELFSPEC, k)
+    torch.cuda.synchronize()
+    lora_bytes = shape.n_layers * shape.lora_rank * (shape.n_q_heads * shape.head_dim + shape.d_model) * 2
+    committed = rounds = 0
+    bytes_ = 0.0
+    t0 = time.perf_counter()
+    while committed < n_new:
+        b = sess.forward_bytes(k + 1) + lora_bytes + sess.forward_bytes(k)
+        _, st = sess.decode_step(tm.TRI_SELFSPEC, k)
+        committed += st[0][0]
+        rounds += 1
+        bytes_ += b
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gbs = bytes_ / dt / 1e9
+    print(json.dumps({
+        "metric": "committed tokens/s @bs1, 14B-class self-spec block 32 + draft LoRA r128, 16384-token prefix",
+        "value": round(committed / dt, 3), "unit": "tok/s", "rounds": rounds, "committed": committed,
+        "tpf": round(committed / (2 * rounds), 4), "ms_per_round": round(dt * 1e3 / rounds, 3),
+        "forward_ms": round(dt * 1e3 / (2 * rounds), 3), "prefill_s": round(prefill_s, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "note": "algorithmic bytes of both forwards of a round: weights, KV of the prefix, "
+                             "LoRA of the draft forward, logits"},
+        "data": "synthetic (seeded random-init weights and LoRA, uniform random prefix)"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,10 +529,16 @@ def main():
     ap.add_argument("--no-replay", action="store_true")
     ap.add_argument("--attn", action="store_true",
                     help="time block_causal_attn alone at the attention-only shapes instead of the decode round")
+    ap.add_argument("--attn-splits", action="store_true",
+                    help="block_causal_attn alone at 4K..32K keys with every key split forced")
     ap.add_argument("--concurrency", action="store_true",
                     help="mixed AR / self-speculation steps at 1..64 sequences with the mode choice by concurrency")
     ap.add_argument("--sol", action="store_true",
                     help="speed-of-light analysis (serial denoising + parallel pass) at 1 and 8 sequences")
+    ap.add_argument("--diffusion", action="store_true",
+                    help="8B-class diffusion mode at 1/4/16 sequences and thresholds 0.5/0.7/0.9, plus AR at 16")
+    ap.add_argument("--long14b", action="store_true",
+                    help="14B-class self-speculation with the draft LoRA behind a 16384-token prefix")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -360,11 +549,20 @@ def main():
     if args.attn:
         attention_alone(args)
         return
+    if args.attn_splits:
+        attention_split_sweep(args)
+        return
     if args.concurrency:
         concurrency_sweep(args)
         return
     if args.sol:
         sol_analysis(args)
+        return
+    if args.diffusion:
+        diffusion_sweep(args)
+        return
+    if args.long14b:
+        long_prefix_14b(args)
         return
 
     import numpy as np

@@ -259,6 +259,17 @@ int tri_trace_get(tri_session* session, int i, int* n_rows, int32_t* seq, int32_
  * a_star < 0 switches the replay off.  ref is copied (host, n_ref ids). */
 int tri_set_draft_override(tri_session* session, int seq, const int32_t* ref, int n_ref, int a_star);
 
+/* Controlled commit rate of diffusion mode: while set (n > 0), the t-th
+ * forward of each diffusion block of `seq` commits the min(counts[t % n],
+ * remaining) most confident masked positions (lowest position on ties) with
+ * their greedy tokens, in place of the threshold rule; every forward still
+ * runs in full.  A stand-in for a trained sampler's commit rate (the pages
+ * report about 2.6x TPF for diffusion mode, [Blog] performance highlights)
+ * on random-init weights, whose confidences never pass a threshold.
+ * counts: host, n entries >= 1, copied; n = 0 switches it off.  tri_prefill
+ * of the sequence switches it off too.  TRI_EINVAL on a bad schedule. */
+int tri_set_commit_schedule(tri_session* session, int seq, const int32_t* counts, int n);
+
 /* Time every launch of one kernel class with HIP events on the session stream:
  * 0 gate/up GEMM, 1 down GEMM, 2 QKV GEMM, 3 o_proj GEMM, 4 lm_head GEMM,
  * 5 attention (+ split combine), 6 whole forward; -1 switches timing off.

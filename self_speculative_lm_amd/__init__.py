@@ -210,6 +210,15 @@ class Session:
             out.append(a)
         return out
 
+    def set_commit_schedule(self, seq: int, counts=None) -> None:
+        """Diffusion forwards of `seq` commit counts[t % len] most confident
+        positions (None or empty: the threshold rule again)."""
+        if not counts:
+            check(lib().tri_set_commit_schedule(self.handle, seq, None, 0))
+            return
+        c = _i32(counts)
+        check(lib().tri_set_commit_schedule(self.handle, seq, _ip(c), len(c)))
+
     def set_draft_override(self, seq: int, ref=None, a_star: int = -1) -> None:
         if a_star < 0 or ref is None:
             check(lib().tri_set_draft_override(self.handle, seq, None, 0, -1))

@@ -62,6 +62,7 @@ SIGNATURES = {
     "tri_trace_count": (I, [P, ctypes.POINTER(I)]),
     "tri_trace_get": (I, [P, I, ctypes.POINTER(I), IP, IP, IP, IP, IP, FP, I, ctypes.POINTER(I)]),
     "tri_set_draft_override": (I, [P, I, IP, I, I]),
+    "tri_set_commit_schedule": (I, [P, I, IP, I]),
     "tri_profile": (I, [P, I]),
     "tri_profile_read": (I, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]),
     "block_causal_attn_ws_bytes": (I, [I, I, I, I, I, ctypes.POINTER(SZ)]),

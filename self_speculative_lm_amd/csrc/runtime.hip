@@ -73,6 +73,8 @@ struct Seq {
   // controlled-acceptance override (benchmark hook)
   std::vector<int32_t> ref;
   int a_star = -1;
+  // controlled commit rate (benchmark hook): per-forward commit counts of a diffusion block
+  std::vector<int32_t> sched;
 };
 
 // Row metadata of one forward: a host (pinned) mirror and a device copy.
@@ -513,7 +515,7 @@ int step_ar(tri_session* s, const std::vector<int>& act, int stride, int32_t* ou
 
 // order (optional): the positions of each block in the order they were committed.
 int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau, int stride, int32_t* out_tokens,
-                   tri_seq_stats* st, std::vector<std::vector<int>>* order = nullptr) {
+                   tri_seq_stats* st, std::vector<std::vector<int>>* order = nullptr, bool use_sched = true) {
   const int mask = s->m->d.vocab;
   const size_t na = act.size();
   std::vector<std::vector<int32_t>> y(na, std::vector<int32_t>(B, mask));
@@ -548,6 +550,19 @@ int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau
     if (s->hints[s->o_status]) return fail(TRI_ENUMERIC, "non-finite logits in diffusion step");
     for (size_t j = 0; j < na; ++j) {
       if (blk_row[j] < 0) continue;
+      const std::vector<int32_t>& sched = s->seqs[act[j]].sched;
+      if (use_sched && !sched.empty()) {
+        // the n most confident masked positions (lowest position on ties)
+        // replace the threshold rule's commits
+        std::vector<int> cand;
+        for (int i = 0; i < B; ++i)
+          if (!done[j][i]) cand.push_back(i);
+        const float* cf = s->hconf + blk_row[j];
+        std::stable_sort(cand.begin(), cand.end(), [&](int a, int b) { return cf[a] > cf[b]; });
+        const size_t n = std::min<size_t>(cand.size(), (size_t)sched[fwd[j] % sched.size()]);
+        for (int i = 0; i < B; ++i) s->hints[s->o_out_commit + blk_row[j] + i] = 0;
+        for (size_t c = 0; c < n; ++c) s->hints[s->o_out_commit + blk_row[j] + cand[c]] = 1;
+      }
       ++fwd[j];
       for (int i = 0; i < B; ++i) {
         const int r = blk_row[j] + i;
@@ -1101,6 +1116,7 @@ int tri_prefill(tri_session* s, int seq, const int32_t* tokens, int n) {
   S.active = true;
   S.a_star = -1;
   S.ref.clear();
+  S.sched.clear();
   for (int b = 0; b < n - 1; b += s->max_rows) {
     const int e = std::min(n - 1, b + s->max_rows);
     HostRows R;
@@ -1226,7 +1242,7 @@ int tri_sol_block(tri_session* s, int block, int32_t* out_target, int32_t* out_o
   // position per forward (no confidence exceeds 1)
   std::vector<int32_t> toks(cells + (size_t)s->max_batch, -1);
   std::vector<std::vector<int>> order(na);
-  int rc = step_diffusion(s, act, block, 1.f, block, toks.data(), nullptr, &order);
+  int rc = step_diffusion(s, act, block, 1.f, block, toks.data(), nullptr, &order, false);
   if (rc) return rc;
   std::vector<std::vector<int32_t>> target(na);
   for (size_t j = 0; j < na; ++j) {
@@ -1427,6 +1443,16 @@ int tri_trace_get(tri_session* s, int i, int* n_rows, int32_t* seq, int32_t* tok
   if (hi) memcpy(hi, r.hi.data(), n * 4);
   if (lora) memcpy(lora, r.lora.data(), n * 4);
   if (logits && !r.logits.empty()) memcpy(logits, r.logits.data(), r.logits.size() * 4);
+  return TRI_OK;
+}
+
+int tri_set_commit_schedule(tri_session* s, int seq, const int32_t* counts, int n) {
+  int rc = check_seq(s, seq);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && !counts)) return fail(TRI_EINVAL, "bad commit schedule");
+  for (int i = 0; i < n; ++i)
+    if (counts[i] < 1) return fail(TRI_EINVAL, "commit count %d of the schedule is below 1", i);
+  s->seqs[seq].sched.assign(counts, counts + n);
   return TRI_OK;
 }
 

@@ -411,3 +411,47 @@ def test_state_errors_and_kv_bookkeeping():
     s2.prefill(0, seeded.prompt(30, shape.vocab))
     out2, _ = s2.decode_step(tm.TRI_AR, 1)
     assert out2[0, 0] == out[0, 0]
+
+
+def test_tiny_scheduled_commit_rate_matches_oracle():
+    """The controlled commit rate of diffusion mode: a scheduled sequence
+    commits the oracle's top-n positions per forward while a sequence in the
+    same forwards keeps the threshold rule; a prefill switches the schedule off."""
+    import self_speculative_lm_amd as tm
+    shape = seeded.TINY_SHARP
+    _, _, model, om = get(shape)
+    prompts = [seeded.prompt(n, shape.vocab, stream=70 + i) for i, n in enumerate((16, 11, 13))]
+    counts = [[3, 1, 2], None, [2]]
+    sess = tm.Session(model, max_batch=3, max_ctx=96, max_rows=3 * 24)
+    sess.set_trace(True)
+    for i, p in enumerate(prompts):
+        sess.prefill(i, p)
+        if counts[i]:
+            sess.set_commit_schedule(i, counts[i])
+    got = [[] for _ in prompts]
+    fw = [[] for _ in prompts]
+    for _ in range(3):
+        toks, st = sess.decode_step(tm.TRI_DIFFUSION, 8, 0.9)
+        for i in range(3):
+            got[i] += toks[i][:8].tolist()
+            fw[i].append(st[i][1])
+    for i, p in enumerate(prompts):
+        o = OracleSession(om, 96)
+        o.prefill(p)
+        want, wf = [], []
+        for _ in range(3):
+            f0 = o.forwards
+            want += o.diffusion_block_scheduled(8, counts[i]) if counts[i] else o.diffusion_block(8, 0.9)
+            wf.append(o.forwards - f0)
+        assert got[i] == want, i
+        assert fw[i] == wf, i
+    assert fw[0] == [4, 4, 4] and fw[2] == [4, 4, 4]
+    err, _, _ = teacher_forced_error(shape, sess, max_ctx=96)
+    assert err <= TOL_F32, err
+    sess.prefill(0, prompts[0])                          # the schedule is gone
+    toks, _ = sess.decode_step(tm.TRI_DIFFUSION, 8, 0.9)
+    o = OracleSession(om, 96)
+    o.prefill(prompts[0])
+    assert toks[0][:8].tolist() == o.diffusion_block(8, 0.9)
+    with pytest.raises(tm.TriError):
+        sess.set_commit_schedule(0, [2, 0])

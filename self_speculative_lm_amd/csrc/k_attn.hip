@@ -519,7 +519,7 @@ static void attn_shape(int qtiles, int max_hi, int* qw, int* qt) {
     *qt = max_hi > 1024 ? 2 : 1;
     return;
   }
-  *qt = (qtiles > 8 && max_hi > 4096) ? 2 : 1;
+  *qt = (qtiles >= 8 && max_hi > 4096) ? 2 : 1;
   *qw = (*qt == 1 && (qtiles <= 2 || max_hi <= 1536)) ? 2 : 4;
 }
 
@@ -543,19 +543,23 @@ int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int 
   // measurements at 32q/8kv heads, 32-row blocks, prefixes 512..32K, 1 and 8
   // sequences: a workgroup costs 4 us plus 1.8 us per 128 keys it walks (two
   // key groups of 64-key tiles), workgroups run one per CU in waves of 256,
-  // and more than one split adds a 4 us combine.
+  // and more than one split adds a 4 us combine.  Workgroups of two query
+  // tiles per wave (long prefixes) were fitted separately, at prefixes 4K..32K:
+  // 13 us plus 2.8 us per 128 keys, no measurable combine term.
   const int G = hkv > 0 ? hq / hkv : 1;
   const int qtiles = std::max(1, (rows_per_seq * G + 15) / 16);
   int qw, qt;
   attn_shape(qtiles, max_hi, &qw, &qt);
   const long qg = (qtiles + qw * qt - 1) / (qw * qt);
+  const double fixed = qt == 2 ? 13.0 : 4.0, per128 = qt == 2 ? 2.8 : 1.8, combine = qt == 2 ? 0.0 : 4.0;
   int best = 128;
   double bt = 1e30;
   for (int sp = 128; sp <= 4096; sp *= 2) {
     const long ns = std::max(1, (max_hi + sp - 1) / sp);
     const long nwg = ns * qg * std::max(1, n_seq) * std::max(1, hkv);
-    const double t = std::ceil(nwg / 256.0) * (4.0 + 1.8 * std::ceil(std::min(sp, std::max(max_hi, 1)) / 128.0)) +
-                     (ns > 1 ? 4.0 : 0.0);
+    const double t =
+        std::ceil(nwg / 256.0) * (fixed + per128 * std::ceil(std::min(sp, std::max(max_hi, 1)) / 128.0)) +
+        (ns > 1 ? combine : 0.0);
     if (t < bt) {
       bt = t;
       best = sp;

@@ -61,6 +61,7 @@ struct AttnArgs {
   bf16_t* out;
   float* part_o;   // [nsplit][rows][hq][HD]
   float* part_ml;  // [nsplit][rows][hq][2]
+  int qgroups, nz;  // query groups per (split, sequence x kv head); n_seq * hkv
 };
 
 __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
@@ -107,14 +108,21 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = wave / QW, qs = wave - kg * QW;  // key group, query slot
   const int tg = tid - kg * GTH;                  // thread index inside the key group
-  const int seq = blockIdx.z / a.hkv, kvh = blockIdx.z - seq * a.hkv;
+  // Workgroup id -> (split bx, query group bq, sequence x kv head bz).  The
+  // query groups of one (split, kv head) get ids 8 apart, so they run on one
+  // XCD one after the other and the later ones find the K/V tiles in its L2.
+  const int per = 8 * a.qgroups;
+  const int pr = ((int)blockIdx.x / per) * 8 + ((int)blockIdx.x & 7);
+  if (pr >= a.nsplit * a.nz) return;
+  const int bq = ((int)blockIdx.x % per) >> 3, bx = pr % a.nsplit, bz = pr / a.nsplit;
+  const int seq = bz / a.hkv, kvh = bz - seq * a.hkv;
   const int G = a.hq / a.hkv;
   const int cseq = a.slot_seq ? a.slot_seq[seq] : seq;
   const int r0 = a.seq_start[seq];
   const int nq = (a.seq_start[seq + 1] - r0) * G;
-  const int qbase = blockIdx.y * (QW * 16 * QT);
+  const int qbase = bq * (QW * 16 * QT);
   if (qbase >= nq) return;
-  const int kbeg = blockIdx.x * a.kv_split;
+  const int kbeg = bx * a.kv_split;
   const bf16_t* kbase = a.kc + (size_t)(cseq * a.hkv + kvh) * a.ctx * HD;
   const bf16_t* vbase = a.vc + (size_t)(cseq * a.hkv + kvh) * HD * a.ctx;
 
@@ -398,7 +406,7 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(lo, hi);
       }
     } else {
-      const size_t base = ((size_t)blockIdx.x * a.rows + qrow(q)) * a.hq + qhead(q);
+      const size_t base = ((size_t)bx * a.rows + qrow(q)) * a.hq + qhead(q);
       float* po = a.part_o + base * HD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = oacc[q][dt];
@@ -608,7 +616,11 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   int qw, qt;
   attn_shape(qtiles, L.max_hi, &qw, &qt);
   const int qgroups = (qtiles + qw * qt - 1) / (qw * qt);
-  dim3 grid(a.nsplit, qgroups, L.n_seq * L.hkv);
+  a.qgroups = qgroups;
+  a.nz = L.n_seq * L.hkv;
+  const long pairs8 = ((long)a.nsplit * a.nz + 7) / 8 * 8;
+  if (pairs8 * qgroups > 0x7fffffffL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(pairs8 * qgroups));
   if (qw == 2)
     hipLaunchKernelGGL((attn_bf16_kernel<2, 2, 1>), grid, dim3(256), 0, st, a);
   else if (qt == 1)

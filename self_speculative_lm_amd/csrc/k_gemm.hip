@@ -519,6 +519,13 @@ bool gemm_use_big(int M, int N, int K) { return M > 64 && (M >= 256 || N >= 1638
 // (up to 40% of the bf16 MFMA peak on the down projection).
 constexpr int BIGM_MT = 4, BIGM_D = 4, BIGM_FPW = 4, BIGM_WAVES = 8;
 constexpr int BIGM_BPW = BIGM_WAVES * BIGM_FPW / 8;  // packed blocks per workgroup
+// Tall form for 65..128 rows: one 128-row tile (8 row tiles) x 2 fragments
+// per wave, so W is streamed once for all the rows instead of once per
+// 64-row tile.  Its per-split partials have the same bits as the other
+// forms (same MFMA, same k order per element).
+constexpr int TALL_MT = 8, TALL_FPW = 2;
+constexpr int TALL_BPW = BIGM_WAVES * TALL_FPW / 8;
+__host__ __forceinline__ bool big_tall(int M) { return M <= TALL_MT * 16; }
 
 // Large-M grid: as few K-split groups (output slots) as keep >= 192
 // workgroups in flight, otherwise one group per packed split.  With
@@ -530,8 +537,9 @@ constexpr int BIGM_BPW = BIGM_WAVES * BIGM_FPW / 8;  // packed blocks per workgr
 // in a different order.
 static BigGrid big_grid(const GemmPlan& p, int M, int N, bool invariant) {
   BigGrid g;
-  g.ntm = (M + BIGM_MT * 16 - 1) / (BIGM_MT * 16);
-  const int nfg8 = (((N + GROUP - 1) / GROUP + BIGM_BPW - 1) / BIGM_BPW + 7) / 8 * 8;
+  const int rows = big_tall(M) ? TALL_MT * 16 : BIGM_MT * 16, bpw = big_tall(M) ? TALL_BPW : BIGM_BPW;
+  g.ntm = (M + rows - 1) / rows;
+  const int nfg8 = (((N + GROUP - 1) / GROUP + bpw - 1) / bpw + 7) / 8 * 8;
   g.nyg = p.S;
   for (int c = 1; c <= p.S; ++c)
     if (p.S % c == 0 && nfg8 * g.ntm * c >= 192) {
@@ -543,19 +551,25 @@ static BigGrid big_grid(const GemmPlan& p, int M, int N, bool invariant) {
   return g;
 }
 
-template <int NCH>
-void launch_wide(const GemmArgs& a, const BigGrid& g, bool chain, bool swiglu, hipStream_t st) {
+template <int MT, int NCH, int FPW>
+void launch_wide_form(const GemmArgs& a, const BigGrid& g, bool chain, bool swiglu, hipStream_t st) {
   const dim3 grid(a.ntiles), block(BIGM_WAVES * 64);
   if (chain && swiglu)
-    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, true, true>), grid, block, 0, st,
-                       a, g);
+    hipLaunchKernelGGL((gemm_wide_kernel<MT, NCH, BIGM_D, FPW, BIGM_WAVES, true, true>), grid, block, 0, st, a, g);
   else if (chain)
-    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, true>), grid, block, 0, st, a, g);
+    hipLaunchKernelGGL((gemm_wide_kernel<MT, NCH, BIGM_D, FPW, BIGM_WAVES, true>), grid, block, 0, st, a, g);
   else if (swiglu)
-    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, false, true>), grid, block, 0, st,
-                       a, g);
+    hipLaunchKernelGGL((gemm_wide_kernel<MT, NCH, BIGM_D, FPW, BIGM_WAVES, false, true>), grid, block, 0, st, a, g);
   else
-    hipLaunchKernelGGL((gemm_wide_kernel<BIGM_MT, NCH, BIGM_D, BIGM_FPW, BIGM_WAVES, false>), grid, block, 0, st, a, g);
+    hipLaunchKernelGGL((gemm_wide_kernel<MT, NCH, BIGM_D, FPW, BIGM_WAVES, false>), grid, block, 0, st, a, g);
+}
+
+template <int NCH>
+void launch_wide(const GemmArgs& a, const BigGrid& g, bool chain, bool swiglu, bool tall, hipStream_t st) {
+  if (tall)
+    launch_wide_form<TALL_MT, NCH, TALL_FPW>(a, g, chain, swiglu, st);
+  else
+    launch_wide_form<BIGM_MT, NCH, BIGM_FPW>(a, g, chain, swiglu, st);
 }
 
 int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant) {
@@ -586,7 +600,9 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
       a.S = plan.S;
       a.nfb = (N + GROUP - 1) / GROUP;
       const BigGrid g = big_grid(plan, M, N, invariant);
-      a.ntiles = ((a.nfb + BIGM_BPW - 1) / BIGM_BPW + 7) / 8 * 8 * g.ntm * g.nyg;
+      const bool tall = big_tall(M);
+      const int bpw = tall ? TALL_BPW : BIGM_BPW;
+      a.ntiles = ((a.nfb + bpw - 1) / bpw + 7) / 8 * 8 * g.ntm * g.nyg;
       // passes as long as possible: the largest NCH <= 8 dividing the stages
       // per split (one pass per split for every 8B/14B projection plan)
       const int ps = plan.Ks / KC;
@@ -598,13 +614,13 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
         }
       const bool chain = invariant && g.cs > 1, sw = swiglu_out != nullptr;
       switch (nch) {
-        case 1: launch_wide<1>(a, g, chain, sw, st); break;
-        case 2: launch_wide<2>(a, g, chain, sw, st); break;
-        case 3: launch_wide<3>(a, g, chain, sw, st); break;
-        case 4: launch_wide<4>(a, g, chain, sw, st); break;
-        case 5: launch_wide<5>(a, g, chain, sw, st); break;
-        case 6: launch_wide<6>(a, g, chain, sw, st); break;
-        case 8: launch_wide<8>(a, g, chain, sw, st); break;
+        case 1: launch_wide<1>(a, g, chain, sw, tall, st); break;
+        case 2: launch_wide<2>(a, g, chain, sw, tall, st); break;
+        case 3: launch_wide<3>(a, g, chain, sw, tall, st); break;
+        case 4: launch_wide<4>(a, g, chain, sw, tall, st); break;
+        case 5: launch_wide<5>(a, g, chain, sw, tall, st); break;
+        case 6: launch_wide<6>(a, g, chain, sw, tall, st); break;
+        case 8: launch_wide<8>(a, g, chain, sw, tall, st); break;
         default: return hipErrorInvalidValue;
       }
       return hipGetLastError();

@@ -157,3 +157,38 @@ def test_8b_shape_mixed_batch_teacher_forced_and_equals_ar():
         ar, _ = run(model, AR, 1, [p], len(outs[i]), max_ctx)
         assert outs[i] == ar[0][: len(outs[i])], i
     check_teacher_forced(S8, oms, sess, max_ctx, prompts)
+
+
+def test_8b_shape_rows_bit_identical_alone_and_in_a_tall_batch():
+    """Three sequences in self-speculation together (99 draft rows, 96 verify
+    rows: the 128-row form of the large-M GEMM on the wide and long-K
+    projections) give bit-identical logits for every row, and the same tokens,
+    as each sequence stepped alone (33 / 32 rows: the decode kernel)."""
+    import self_speculative_lm_amd as tm
+    model, *oms = get(S8)
+    prompts = [seeded.prompt(40 + 9 * i, S8.vocab, stream=140 + i) for i in range(3)]
+    sessions = []
+    for _ in range(2):
+        sess = tm.Session(model, max_batch=3, max_ctx=256, max_rows=3 * 34)
+        for i, p in enumerate(prompts):
+            sess.prefill(i, p)
+        sess.set_trace(True)
+        sessions.append(sess)
+    together, alone = sessions
+    SS = tm.TRI_SELFSPEC
+    for step in range(2):
+        out_t, _ = together.decode_step_mixed([SS] * 3, 32)
+        for i in range(3):
+            out_a, _ = alone.decode_step_mixed([SS if j == i else -1 for j in range(3)], 32)
+            assert (out_a[i] == out_t[i]).all(), (step, i)
+    tr_t, tr_a = together.trace(), alone.trace()
+    assert len(tr_a) == 3 * len(tr_t)
+    for f, rec in enumerate(tr_t):
+        assert 65 <= len(rec["seq"]) <= 128
+        step, which = divmod(f, 2)
+        for i in range(3):
+            solo = tr_a[(step * 3 + i) * 2 + which]
+            rows = rec["seq"] == i
+            for key in ("tok", "pos", "hi"):
+                assert (rec[key][rows] == solo[key]).all()
+            assert np.array_equal(rec["logits"][rows], solo["logits"]), (f, i)

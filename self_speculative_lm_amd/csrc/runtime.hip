@@ -203,7 +203,7 @@ SessionLayout session_layout(const tri_model* m, int max_batch, int max_ctx, int
   const tri_model_desc& d = m->d;
   SessionLayout S;
   S.ctx = (max_ctx + 63) / 64 * 64;
-  S.kv_split = attn_pick_split(S.ctx, max_batch);
+  S.kv_split = attn_pick_split(S.ctx, max_batch, d.n_q_heads, d.n_kv_heads);
   S.css = (size_t)d.n_kv_heads * S.ctx * d.head_dim;
   const size_t cache_bytes = (size_t)d.n_layers * max_batch * S.css * m->esz;
   const size_t qd = (size_t)d.n_q_heads * d.head_dim;

@@ -126,7 +126,7 @@ struct AttnLaunch {
   void* out;
   float* part;  // split partials
 };
-int attn_pick_split(int max_ctx, int n_seq);
+int attn_pick_split(int max_ctx, int n_seq, int hq, int hkv);
 int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int hkv);
 size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split);
 hipError_t launch_attn(int dtype, const AttnLaunch& a, hipStream_t st);

@@ -153,9 +153,16 @@ def test_8b_shape_mixed_batch_teacher_forced_and_equals_ar():
             got = [int(t) for t in toks[i] if t >= 0]
             assert len(got) == (2 if m == AR else st[i][2] + 1)
             outs[i] += got
+    # AR references in a session of the same shape (six slots, one prefilled),
+    # so that the attention key split is the mixed session's
     for i, p in enumerate(prompts):
-        ar, _ = run(model, AR, 1, [p], len(outs[i]), max_ctx)
-        assert outs[i] == ar[0][: len(outs[i])], i
+        ref = tm.Session(model, max_batch=6, max_ctx=max_ctx, max_rows=6 * 34)
+        ref.prefill(i, p)
+        ar = []
+        while len(ar) < len(outs[i]):
+            toks, _ = ref.decode_step(AR, 1)
+            ar.append(int(toks[i][0]))
+        assert outs[i] == ar, i
     check_teacher_forced(S8, oms, sess, max_ctx, prompts)
 
 

@@ -282,7 +282,8 @@ def test_small_bf16_lora_mixed_batch_lossless():
              [MODE_AR, -1, MODE_SELFSPEC, MODE_SELFSPEC, -1, MODE_AR]]
     got, _, sess = gpu_mixed(shape, prompts, sched, 32, lora=True, trace=True)
     n = min(len(g) for g in got)
-    ar, _, _ = gpu_generate(shape, MODE_AR, n, 1, prompts=prompts)
+    # the same session shape (sequences, capacity), so the same key split
+    ar, _, _ = gpu_generate(shape, MODE_AR, n, 1, prompts=prompts, max_ctx=200)
     for i in range(len(prompts)):
         assert got[i][:n] == ar[i], i
     err, tr, _ = teacher_forced_error(shape, sess, max_ctx=200)

@@ -169,48 +169,51 @@ def attention_alone(args):
 
 
 def attention_split_sweep(args):
-    """Block-causal attention alone at prefixes 4K..32K, batch 1 and 8, with the
-    key split forced to each power of two in [256, 4096] and the library's own
-    pick (0): one JSON line per (prefix, batch), microseconds per launch (HIP
-    events around 30 back-to-back calls).  The data behind the split cost model."""
+    """Block-causal attention alone with the key split forced to each power of
+    two and the library's own pick (0): prefixes 512..2K at 1, 2, 4 and 16
+    sequences (splits 128..2048), then 4K..32K at 1 and 8 (splits 256..4096).
+    One JSON line per (prefix, batch), microseconds per launch (HIP events
+    around 30 back-to-back calls).  The data behind the split cost model and
+    the session split rule."""
     import torch
     import self_speculative_lm_amd as tm
     dev = "cuda:0"
     torch.cuda.set_device(0)
     hq, hkv, hd, nb = 32, 8, 128, 32
     g = torch.Generator(device=dev).manual_seed(3)
-    for P in (4096, 8192, 16384, 32768):
-        for b in (1, 8):
-            L = P + nb
-            ctx = (L + 63) // 64 * 64
-            kc = torch.randn((b, hkv, ctx, hd), generator=g, device=dev).to(torch.bfloat16)
-            vc = torch.randn((b, hkv, hd, ctx), generator=g, device=dev).to(torch.bfloat16)
-            q = torch.randn((b * nb, hq, hd), generator=g, device=dev).to(torch.bfloat16)
-            out = torch.empty_like(q)
-            ss = torch.arange(0, b * nb + 1, nb, dtype=torch.int32, device=dev)
-            hi = torch.full((b * nb,), L, dtype=torch.int32, device=dev)
-            res = {}
-            for sp in (0, 256, 512, 1024, 2048, 4096):
-                ws = torch.empty(tm.block_causal_attn_ws_bytes(b * nb, hq, hd, L, sp), dtype=torch.uint8, device=dev)
+    grid = [(P, b, (0, 128, 256, 512, 1024, 2048)) for P in (512, 1024, 2048) for b in (1, 2, 4, 16)]
+    grid += [(P, b, (0, 256, 512, 1024, 2048, 4096)) for P in (4096, 8192, 16384, 32768) for b in (1, 8)]
+    for P, b, splits in grid:
+        L = P + nb
+        ctx = (L + 63) // 64 * 64
+        kc = torch.randn((b, hkv, ctx, hd), generator=g, device=dev).to(torch.bfloat16)
+        vc = torch.randn((b, hkv, hd, ctx), generator=g, device=dev).to(torch.bfloat16)
+        q = torch.randn((b * nb, hq, hd), generator=g, device=dev).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ss = torch.arange(0, b * nb + 1, nb, dtype=torch.int32, device=dev)
+        hi = torch.full((b * nb,), L, dtype=torch.int32, device=dev)
+        res = {}
+        for sp in splits:
+            ws = torch.empty(tm.block_causal_attn_ws_bytes(b * nb, hq, hd, L, sp), dtype=torch.uint8, device=dev)
 
-                def run():
-                    tm.block_causal_attn(q, kc, vc, ss, hi, out, 1.0 / math.sqrt(hd), max_rows_per_seq=nb,
-                                         max_hi=L, kv_split=sp, ws=ws)
-                for _ in range(3):
-                    run()
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(30):
-                    run()
-                e1.record()
-                torch.cuda.synchronize()
-                res[sp] = round(e0.elapsed_time(e1) * 1e3 / 30, 2)
-                del ws
-            print(json.dumps({"metric": "block-causal attention alone, us by key split", "prefix": P, "batch": b,
-                              "us_by_split": res}), flush=True)
-            del kc, vc, q, out
-            torch.cuda.empty_cache()
+            def run():
+                tm.block_causal_attn(q, kc, vc, ss, hi, out, 1.0 / math.sqrt(hd), max_rows_per_seq=nb,
+                                     max_hi=L, kv_split=sp, ws=ws)
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(30):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            res[sp] = round(e0.elapsed_time(e1) * 1e3 / 30, 2)
+            del ws
+        print(json.dumps({"metric": "block-causal attention alone, us by key split", "prefix": P, "batch": b,
+                          "us_by_split": res}), flush=True)
+        del kc, vc, q, out
+        torch.cuda.empty_cache()
 
 
 def build_model(shape, dev):

@@ -533,19 +533,19 @@ static void attn_shape(int qtiles, int max_hi, int* qw, int* qt) {
 
 int attn_pick_split(int max_ctx, int n_seq, int hq, int hkv) {
   // Keys per split for a session of n_seq sequences of up to max_ctx keys.
-  // One sequence: the largest power of two at most max_ctx / 32, within
-  // [128, 2048].  Measured on MI355X for 33-row decode forwards at batch 1
-  // (attention + combine, two key groups per workgroup): 600 keys 12 us with
-  // 128-key splits, 2K keys 15 us with 256, 8K keys 25 us with 1024; a
-  // session's contexts usually stay well below its capacity, which short
-  // splits suit.  Several sequences: the launch model below at the session's
+  // One sequence: the largest power of two at most max_ctx / 16, within
+  // [128, 2048].  Measured on MI355X for 32-row blocks at batch 1 (attention
+  // + combine): 1K keys 12.0 us with 256-key splits (15.6 with 128), 2K keys
+  // 13.9 with 256, 8K keys 24.7 with 512, 16K keys 32.8 with 1024; a
+  // session's contexts usually stay below its capacity, which the shorter
+  // splits also serve.  Several sequences: the launch model below at the session's
   // capacity and a 33-row block per sequence (their workgroups fill the chip
   // without short splits: at 4 sequences x 1K keys 22 us unsplit against 34
   // with 128-key splits, at 16 x 1K 43 against 111).  A session keeps one
   // split size, so a row's result never depends on the launch.
   if (n_seq > 1) return attn_pick_split_launch(max_ctx, n_seq, 33, hq, hkv);
   int s = 128;
-  const double lim = (double)max_ctx / 32.0;
+  const double lim = (double)max_ctx / 16.0;
   while (s < 2048 && 2.0 * s <= lim) s *= 2;
   return s;
 }

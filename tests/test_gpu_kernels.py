@@ -78,8 +78,17 @@ def test_block_causal_attn_bf16_matches_oracle(prefixes, nrows, causal, kv_split
     assert err <= ATT_TOL_BF16, err
 
 
-def test_block_causal_attn_bf16_group5():
-    assert _attn_case([100], [33], 40, 8, 128, True, False, 64) <= ATT_TOL_BF16
+@pytest.mark.parametrize("prefixes,nrows,kv_split", [
+    ([100], [33], 64),
+    ([6000], [33], 0),                  # 165 query vectors past 4K keys: two query groups of two tiles per wave
+    ([5000, 700, 4200], [33, 32, 5], 1024),   # three sequences, query groups 8 workgroup ids apart
+])
+def test_block_causal_attn_bf16_group5(prefixes, nrows, kv_split):
+    """Five query heads per kv head (the 14B-class head layout)."""
+    rng = np.random.default_rng(sum(prefixes))
+    n = sum(nrows)
+    sample = sorted(set(rng.integers(0, n, 8).tolist() + [0, n - 1]))
+    assert _attn_case(prefixes, nrows, 40, 8, 128, True, False, kv_split, sample=sample) <= ATT_TOL_BF16
 
 
 @pytest.mark.parametrize("prefix,nrows,kv_split", [(600, 33, 256), (5000, 33, 512), (130, 40, 64), (6000, 33, 4096),

@@ -108,7 +108,9 @@ int tri_model_destroy(tri_model* model);
  * allocated, >= 256-byte aligned) that tri_session_create carves into the KV
  * caches and scratch buffers.  The session launches everything on `stream`.
  * KV cache layout (per layer, per sequence): K [hkv][ctx][hd], V transposed
- * [hkv][hd][ctx], ctx = max_ctx rounded up to a multiple of 64.
+ * [hkv][hd][ctx], ctx = max_ctx rounded up to a multiple of 64.  bf16 models
+ * store K as bf16 and V as the fp16 the attention multiplies: each value
+ * rounded to bf16, then converted to fp16 with saturation at +-65504.
  * ------------------------------------------------------------------------ */
 int tri_session_bytes(const tri_model* model, int max_batch, int max_ctx, int max_rows,
                       size_t* bytes);

@@ -97,7 +97,9 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // group without a valid key contributes with weight exp2(-1e30 - M) = 0).
 // The tile order inside a key group, and so every rounding, depends only on
 // kv_split and KW, never on the other rows of the launch.
-template <int QW, int KW, int QT>
+// VF16: the V cache already holds the fp16 form of every element (the
+// session writes it so), and staging copies the bits.
+template <int QW, int KW, int QT, bool VF16 = false>
 __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
   constexpr int GTH = QW * 64;         // threads of a key group
   constexpr int PIECES = KT * HD / 8;  // 16-byte pieces of one K (or V^T) tile
@@ -148,8 +150,12 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
       const int i = tg + u * GTH;
       *reinterpret_cast<bf16x8*>(&ks[b][(i >> 4) * KPAD + (i & 15) * 8]) = kr[u];
       f16x8 vv;
+      if constexpr (VF16) {
+        vv = __builtin_bit_cast(f16x8, vr[u]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vv[e] = (_Float16)fminf(fmaxf((float)vr[u][e], -65504.f), 65504.f);
+        for (int e = 0; e < 8; ++e) vv[e] = (_Float16)fminf(fmaxf((float)vr[u][e], -65504.f), 65504.f);
+      }
       if (vlim < KT) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -626,12 +632,20 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   const long pairs8 = ((long)a.nsplit * a.nz + 7) / 8 * 8;
   if (pairs8 * qgroups > 0x7fffffffL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(pairs8 * qgroups));
-  if (qw == 2)
+  if (L.v_f16) {
+    if (qw == 2)
+      hipLaunchKernelGGL((attn_bf16_kernel<2, 2, 1, true>), grid, dim3(256), 0, st, a);
+    else if (qt == 1)
+      hipLaunchKernelGGL((attn_bf16_kernel<4, 2, 1, true>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bf16_kernel<4, 2, 2, true>), grid, dim3(512), 0, st, a);
+  } else if (qw == 2) {
     hipLaunchKernelGGL((attn_bf16_kernel<2, 2, 1>), grid, dim3(256), 0, st, a);
-  else if (qt == 1)
+  } else if (qt == 1) {
     hipLaunchKernelGGL((attn_bf16_kernel<4, 2, 1>), grid, dim3(512), 0, st, a);
-  else
+  } else {
     hipLaunchKernelGGL((attn_bf16_kernel<4, 2, 2>), grid, dim3(512), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(L.rows, (L.hq + 3) / 4), dim3(4 * HD), 0, st, a.part_o, a.part_ml,

@@ -150,12 +150,22 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
   }
 }
 
+// V element as the bf16 attention multiplies it: rounded to bf16 (the cache's
+// storage precision), then converted to fp16 with saturation at +-65504.  A
+// V cache kept in this form spares every attention workgroup that reads a
+// tile the conversion, with the same bits.
+__device__ __forceinline__ bf16_t v_cache_f16(float v) {
+  const _Float16 h = (_Float16)fminf(fmaxf(bf16_to_f32(f32_to_bf16(v)), -65504.f), 65504.f);
+  return __builtin_bit_cast(bf16_t, h);
+}
+
 // The same for head_dim 128 with vector accesses: 16 lanes per head, each
 // lane four consecutive columns of both halves (float4 slot and table loads),
-// four heads per wave.  Same arithmetic per element as rope_kv_kernel.
+// four heads per wave.  Same arithmetic per element as rope_kv_kernel.  VF16
+// (bf16 models): V is written in the attention's fp16 form.
 constexpr int ROPE128_HPW = 4;                    // heads per wave
 constexpr int ROPE128_HEADS = 4 * ROPE128_HPW;    // heads per 256-thread workgroup
-template <typename T>
+template <typename T, bool VF16 = false>
 __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict__ P, int nslots, size_t stride,
                                                          int hq, int hkv, const int32_t* row_seq,
                                                          const int32_t* row_pos, const float* __restrict__ rope,
@@ -194,8 +204,13 @@ __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict
     const size_t o = (size_t)seq * css + (size_t)kh * hd * ctx + pos;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      Elem<T>::store(vc, o + (size_t)(c + e) * ctx, xa[e]);
-      Elem<T>::store(vc, o + (size_t)(c + half + e) * ctx, xb[e]);
+      if constexpr (VF16) {
+        vc[o + (size_t)(c + e) * ctx] = v_cache_f16(xa[e]);
+        vc[o + (size_t)(c + half + e) * ctx] = v_cache_f16(xb[e]);
+      } else {
+        Elem<T>::store(vc, o + (size_t)(c + e) * ctx, xa[e]);
+        Elem<T>::store(vc, o + (size_t)(c + half + e) * ctx, xb[e]);
+      }
     }
   }
 }
@@ -457,9 +472,16 @@ hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, si
 
 hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, int rows, int hq, int hkv,
                           int hd, const int32_t* row_seq, const int32_t* row_pos, const float* rope,
-                          void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st) {
+                          void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st, bool v_f16) {
   if (rows <= 0) return hipSuccess;
-  if (nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  if (nslots > MAX_SLOTS || (v_f16 && (dtype != TRI_BF16 || hd != 128))) return hipErrorInvalidValue;
+  if (v_f16) {
+    const dim3 grid128(rows, (hq + 2 * hkv + ROPE128_HEADS - 1) / ROPE128_HEADS);
+    hipLaunchKernelGGL((rope_kv128_kernel<bf16_t, true>), grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
+                       row_seq, row_pos, rope, static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
+                       static_cast<bf16_t*>(vc), ctx, css);
+    return hipGetLastError();
+  }
   if (hd == 128) {
     const dim3 grid128(rows, (hq + 2 * hkv + ROPE128_HEADS - 1) / ROPE128_HEADS);
     TRI_DISPATCH(dtype,

@@ -368,8 +368,9 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
     {
       const size_t stride = (size_t)n * m->qkv_n;
       PROF(PROF_QKV, launch_gemm(dt, s->ybuf, n, D, L.qkv, m->qkv_n, m->p_qkv, s->part, stride, inv, s->st));
+      // bf16 sessions keep V in the attention's fp16 form (same bits, staged without conversion)
       HIPCHK(launch_rope_kv(dt, s->part, gemm_out_slots(dt, m->p_qkv, n, m->qkv_n, D, inv), stride, n, hq, hkv, hd, dm.seq, dm.pos, s->rope, s->qbuf, kc,
-                            vc, s->ctx, s->css, s->st));
+                            vc, s->ctx, s->css, s->st, dt == TRI_BF16));
     }
     {
       AttnLaunch a;
@@ -397,6 +398,7 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
         while (a.kv_split < 4096 && a.kv_split < max_hi) a.kv_split *= 2;
       a.out = s->abuf;
       a.part = static_cast<float*>(s->attn_ws);
+      a.v_f16 = dt == TRI_BF16;
       PROF(PROF_ATTN, launch_attn(dt, a, s->st));
     }
     int oslots = gemm_out_slots(dt, m->p_o, n, D, qd, inv);

@@ -125,6 +125,7 @@ struct AttnLaunch {
   int kv_split;
   void* out;
   float* part;  // split partials
+  bool v_f16 = false;  // bf16: the V cache holds the fp16 form written by launch_rope_kv(v_f16)
 };
 int attn_pick_split(int max_ctx, int n_seq, int hq, int hkv);
 int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int hkv);
@@ -139,7 +140,7 @@ hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, si
 hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
                           int hq, int hkv, int hd, const int32_t* row_seq, const int32_t* row_pos,
                           const float* rope, void* qout, void* kc, void* vc, int ctx,
-                          size_t cache_seq_stride, hipStream_t st);
+                          size_t cache_seq_stride, hipStream_t st, bool v_f16 = false);
 hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
                          int ffn, void* h, hipStream_t st);
 hipError_t launch_lora_mid(int dtype, const float* P, int nslots, size_t slot_stride, int rows,

@@ -109,7 +109,14 @@ def cpu_baseline(shape, prefix, k, tpr, repeats=5):
     per_layer = times[2] - times[1]
     head = times[1] - per_layer
     round_s = head + shape.n_layers * per_layer
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(tpr / round_s, 4), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "host_cpu_count": os.cpu_count(),
             "sample": (f"float64 oracle (float32-stored weights, batched row products), one draft ({k + 1} rows) + "
                        f"one verify ({k} rows) forward over 1- and 2-layer slices of the 8B-class model with a "
                        f"{prefix}-token cache, {repeats} times each; mean per-layer time {per_layer:.3f}s, "
@@ -590,6 +597,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    # measured device-copy bandwidth (read + write of 1 GiB, HIP events): the
+    # practical reference the HBM fractions are also reported against
+    # (skipped in the counter runs, whose calibration copy must stay the only large one)
+    copy_gbs = float("nan")
+    if not args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 5 * 2 * src.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
+        torch.cuda.empty_cache()
     sess.prefill(0, prompt)  # first use of every kernel; timed again below
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -661,6 +686,8 @@ def main():
         "accept_hist": {str(a): accepts.count(a) for a in sorted(set(accepts))},
         "forward_ms": round(elapsed * 1e3 / forwards, 4),
         "round_hbm_fraction": round(round_gbs / HBM_PEAK_GBS, 4),
+        "device_copy_GBps": round(copy_gbs, 1) if copy_gbs == copy_gbs else None,
+        "round_fraction_of_copy": round(round_gbs / copy_gbs, 4) if copy_gbs == copy_gbs else None,
         "round_algorithmic_GBps": round(round_gbs, 1),
         "prefill_ms": round(prefill_s * 1e3, 2),
         "prefill": {"tokens": npf, "chunk_rows": args.max_rows, "ms": round(prefill_s * 1e3, 2),
@@ -671,6 +698,7 @@ def main():
                      "traffic_unit": "HBM bytes per launch (PMC FETCH_SIZE x2 + WRITE_SIZE, copy-calibrated)",
                      "kernel": "gemm_bf16_kernel (gate/up projection, N=24576, K=4096)",
                      "avg_launch_us": round(gu_avg_ms * 1e3, 2), "launches": gu_n,
+                     "frac_of_device_copy": round(gu_gbs / copy_gbs, 4) if copy_gbs == copy_gbs else None,
                      "algorithmic_bytes_per_launch": int(gu_bytes)},
     }
 

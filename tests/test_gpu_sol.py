@@ -114,3 +114,21 @@ def test_sol_errors_leave_state_unchanged():
     r = sess.sol_block(8)
     assert r["forwards"][1] == -1 and (r["target"][1] == -1).all()
     assert sess.state(0)[0][-8:] == r["target"][0].tolist()
+
+
+def test_sol_ignores_a_commit_schedule():
+    """The serial pass is the threshold-1 rule whatever commit schedule the
+    sequence carries (the schedule is a diffusion-step measurement hook)."""
+    import self_speculative_lm_amd as tm
+    shape = seeded.TINY_SHARP
+    _, _, model, _ = get(shape)
+    p = seeded.prompt(14, shape.vocab, stream=99)
+    outs = []
+    for sched in (None, [3, 2]):
+        sess = tm.Session(model, max_batch=1, max_ctx=96, max_rows=40)
+        sess.prefill(0, p)
+        if sched:
+            sess.set_commit_schedule(0, sched)
+        r = sess.sol_block(8)
+        outs.append((r["target"][0].tolist(), r["order"][0].tolist(), r["step"][0].tolist()))
+    assert outs[0] == outs[1]

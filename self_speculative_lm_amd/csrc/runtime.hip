@@ -792,7 +792,7 @@ int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride
   return step_round(s, act, std::vector<char>(act.size(), 1), k, stride, out_tokens, st);
 }
 
-// Mode choice by concurrency (reading R19 of the oracle): forward cost from
+// Mode choice by concurrency ([Notes] §2 mode table and §11; [Digest], Limitations): forward cost from
 // the measured points, linear between them, the first point's time below
 // the first, the line through the last two beyond the last.
 double cost_ms(const int32_t* gr, const double* gm, int ng, double rows) {

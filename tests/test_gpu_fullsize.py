@@ -199,3 +199,47 @@ def test_8b_shape_rows_bit_identical_alone_and_in_a_tall_batch():
             for key in ("tok", "pos", "hi"):
                 assert (rec[key][rows] == solo[key]).all()
             assert np.array_equal(rec["logits"][rows], solo["logits"]), (f, i)
+
+
+def test_8b_full_depth_selfspec_equals_ar_in_the_bench_configuration():
+    """The whole 36-layer 8B-class model in the benchmark's launch configuration
+    (512-token prompt prefilled as one 511-row chunk, draft block 32, batch 1):
+    a property that holds at any size -- self-speculation commits exactly the
+    greedy AR continuation, with its natural drafts and with drafts replaced by
+    that continuation up to a forced mismatch at a* = 6 (7 tokens per round)
+    and a* = 32 (33 per round).  Weights are generated and uploaded one tensor
+    at a time."""
+    import torch
+    import self_speculative_lm_amd as tm
+    _cache.clear()
+    shape = seeded.MODEL_8B
+    tens = {}
+    for i, (name, _, kind) in enumerate(seeded.weight_specs(shape)):
+        _, a = seeded.gen_weight(shape, i)
+        t = torch.from_numpy(a)
+        tens[name] = (t.to(torch.float32) if kind == "ones" else t.to(torch.bfloat16)).to("cuda")
+        del a, t
+    model = make_model(shape, tens)
+    del tens
+    torch.cuda.empty_cache()
+    prompt = seeded.prompt(512, shape.vocab)
+    max_ctx = 512 + 4 * 33 + 120 + 64
+    sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=512)
+    sess.prefill(0, prompt)
+    while len(sess.state(0)[0]) < 512 + 110:
+        sess.decode_step(tm.TRI_AR, 1)
+    ref = sess.state(0)[0]
+    for a_star in (-1, 6, 32):
+        sess.prefill(0, prompt)
+        if a_star >= 0:
+            sess.set_draft_override(0, ref, a_star)
+        rounds = 3
+        for _ in range(rounds):
+            _, st = sess.decode_step(tm.TRI_SELFSPEC, 32)
+            n, f, acc, _ = st[0]
+            assert f == 2 and n == acc + 1
+            if a_star >= 0:
+                assert acc == a_star, (a_star, acc)
+        got = sess.state(0)[0]
+        assert got == ref[: len(got)], a_star
+        sess.set_draft_override(0, None, -1)

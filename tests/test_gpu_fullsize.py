@@ -243,3 +243,45 @@ def test_8b_full_depth_selfspec_equals_ar_in_the_bench_configuration():
         got = sess.state(0)[0]
         assert got == ref[: len(got)], a_star
         sess.set_draft_override(0, None, -1)
+
+
+def test_14b_full_depth_lora_selfspec_equals_ar_behind_a_16k_prefix():
+    """The whole 40-layer 14B-class model with the rank-128 draft LoRA behind a
+    16384-token prefix (the benchmark's long-prefix configuration): the LoRA
+    changes drafts only, so self-speculation still commits exactly the greedy
+    AR continuation, naturally and with drafts replaced by it up to a forced
+    mismatch at a* = 6."""
+    import torch
+    import self_speculative_lm_amd as tm
+    _cache.clear()
+    shape = seeded.MODEL_14B
+    tens = {}
+    for i, (name, _, kind) in enumerate(seeded.weight_specs(shape)):
+        _, a = seeded.gen_weight(shape, i)
+        t = torch.from_numpy(a)
+        tens[name] = (t.to(torch.float32) if kind == "ones" else t.to(torch.bfloat16)).to("cuda")
+        del a, t
+    model = make_model(shape, tens)
+    del tens
+    torch.cuda.empty_cache()
+    prompt = seeded.prompt(16384, shape.vocab, stream=400)
+    max_ctx = 16384 + 2 * 33 + 40 + 64
+    sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=512)
+    sess.prefill(0, prompt)
+    while len(sess.state(0)[0]) < 16384 + 40:
+        sess.decode_step(tm.TRI_AR, 1)
+    ref = sess.state(0)[0]
+    sess.set_lora(True)
+    for a_star in (-1, 6):
+        sess.prefill(0, prompt)
+        if a_star >= 0:
+            sess.set_draft_override(0, ref, a_star)
+        for _ in range(2):
+            _, st = sess.decode_step(tm.TRI_SELFSPEC, 32)
+            n, f, acc, _ = st[0]
+            assert f == 2 and n == acc + 1
+            if a_star >= 0:
+                assert acc == a_star
+        got = sess.state(0)[0]
+        assert got == ref[: len(got)], a_star
+        sess.set_draft_override(0, None, -1)

@@ -51,6 +51,10 @@ enum { TRI_AR = 0, TRI_DIFFUSION = 1, TRI_SELFSPEC = 2 };
 /* Storage types: weights, activations fed to GEMMs, queries and the KV cache.
  * Accumulation, softmax, the residual stream and logits are always float32. */
 enum { TRI_F32 = 0, TRI_BF16 = 1 };
+/* block_causal_attn only: bf16 q/k/out with the V cache in the fp16 form a
+ * bf16 session keeps (each bf16 value converted to IEEE half; exact for
+ * 6.1e-5 <= |v| <= 65504, half-precision subnormals below). */
+enum { TRI_BF16_V16 = 2 };
 
 /* Decoder shape.  The embedding has vocab+1 rows; token id `vocab` is [MASK]
  * (the block's initial state in diffusion mode [Notes §5.2]).  lm_head has
@@ -295,6 +299,8 @@ int tri_profile_read(tri_session* session, double* total_ms, int* launches);
  *   seq_start device int32 [n_seq+1]: rows of sequence s are [seq_start[s], seq_start[s+1])
  *   row_hi    device int32 [rows], 1 <= hi <= ctx
  *   out      [rows][hq][hd]              dtype
+ *   dtype    TRI_F32, TRI_BF16, or TRI_BF16_V16 (v_cache holds IEEE-half bits;
+ *            the session's own cache form)
  * ctx % 64 == 0.  bf16 needs hd == 128, float32 hd <= 128.  max_rows_per_seq
  * and max_hi bound the launch grid (host values >= the true maxima).
  * kv_split: keys per split-KV work unit, a multiple of 64 (0 = pick).  The

@@ -12,11 +12,11 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from ._lib import (TRI_AR, TRI_BF16, TRI_DIFFUSION, TRI_F32, TRI_SELFSPEC, ModelDesc, SeqStats, TriError,  # noqa: F401
+from ._lib import (TRI_AR, TRI_BF16, TRI_BF16_V16, TRI_DIFFUSION, TRI_F32, TRI_SELFSPEC, ModelDesc, SeqStats, TriError,  # noqa: F401
                    check, lib)
 
 __all__ = ["Model", "Session", "block_causal_attn", "sample_commit", "verify_accept", "weight_names", "choose_modes",
-           "TriError", "TRI_AR", "TRI_DIFFUSION", "TRI_SELFSPEC", "TRI_F32", "TRI_BF16"]
+           "TriError", "TRI_AR", "TRI_DIFFUSION", "TRI_SELFSPEC", "TRI_F32", "TRI_BF16", "TRI_BF16_V16"]
 
 
 def _torch():
@@ -264,12 +264,16 @@ def block_causal_attn_ws_bytes(rows: int, hq: int, hd: int, max_hi: int, kv_spli
 def block_causal_attn(q, k_cache, v_cache, seq_start, row_hi, out, scale: float, *, max_rows_per_seq: int,
                       max_hi: int, kv_split: int = 0, ws=None, dtype: Optional[int] = None, stream=None):
     """q [rows, hq, hd]; k_cache [n_seq, hkv, ctx, hd]; v_cache [n_seq, hkv, hd, ctx] (transposed);
-    seq_start int32 [n_seq+1]; row_hi int32 [rows]; out like q.  Device tensors."""
+    seq_start int32 [n_seq+1]; row_hi int32 [rows]; out like q.  Device tensors.  A float16 v_cache
+    with bfloat16 q selects TRI_BF16_V16 (the session's fp16 form of the V cache)."""
     torch = _torch()
     rows, hq, hd = q.shape
     n_seq, hkv, ctx, _ = k_cache.shape
     if dtype is None:
-        dtype = TRI_BF16 if q.dtype == torch.bfloat16 else TRI_F32
+        if q.dtype == torch.bfloat16:
+            dtype = TRI_BF16_V16 if v_cache.dtype == torch.float16 else TRI_BF16
+        else:
+            dtype = TRI_F32
     need = block_causal_attn_ws_bytes(rows, hq, hd, max_hi, kv_split)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -62,18 +62,18 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
 // every k-step the workgroups of a launch read one contiguous window: measured
 // on MI355X this sustains the linear-read rate, whereas one contiguous region
 // per workgroup fell about 10% short.  K is zero-padded to S*Ks.
-// With `il`, the two segments (gate and up, r0 rows each) interleave in
+// PACK_GATEUP: the two segments (gate and up, r0 rows each) interleave in
 // groups of 16 rows: packed rows [32j, 32j+16) are segment 0's rows
 // [16j, 16j+16) and [32j+16, 32j+32) segment 1's, so one MFMA fragment pair
 // holds matching gate and up features.
-__device__ __forceinline__ int pack_row(int row, int r0, bool il) {
-  if (!il) return row;
+__device__ __forceinline__ int pack_row(int row, int r0, int order) {
+  if (order != PACK_GATEUP) return row;
   const int j = row >> 4, w = row & 15;
   return (j & 1) ? r0 + (j >> 1) * 16 + w : (j >> 1) * 16 + w;
 }
 
 __global__ void pack_bf16_kernel(const bf16_t* w0, const bf16_t* w1, const bf16_t* w2, int r0, int r1, int N,
-                                 int K, int nfb, int S, int steps, size_t npieces, bool il, bf16_t* dst) {
+                                 int K, int nfb, int S, int steps, size_t npieces, int il, bf16_t* dst) {
   const int G = nfb * S;
   for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < npieces;
        p += (size_t)gridDim.x * blockDim.x) {
@@ -101,7 +101,7 @@ __global__ void pack_bf16_kernel(const bf16_t* w0, const bf16_t* w1, const bf16_
 
 // float32 models keep row-major weights: the segments are concatenated.
 __global__ void pack_f32_kernel(const float* w0, const float* w1, const float* w2, int r0, int r1, int N, int K,
-                                bool il, float* dst) {
+                                int il, float* dst) {
   const size_t n = (size_t)N * K;
   for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < n; p += (size_t)gridDim.x * blockDim.x) {
     const int prow = (int)(p / K);
@@ -487,8 +487,9 @@ size_t gemm_packed_bytes(const GemmPlan& p, int N, int K, int dtype) {
 }
 
 hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, const GemmPlan& p, void* dst,
-                       bool interleave, hipStream_t st) {
-  if (interleave && (nseg != 2 || segs[0].rows != segs[1].rows || segs[0].rows % 16)) return hipErrorInvalidValue;
+                       int interleave, hipStream_t st) {
+  if (interleave == PACK_GATEUP && (nseg != 2 || segs[0].rows != segs[1].rows || segs[0].rows % 16))
+    return hipErrorInvalidValue;
   const void* w0 = segs[0].ptr;
   const void* w1 = nseg > 1 ? segs[1].ptr : nullptr;
   const void* w2 = nseg > 2 ? segs[2].ptr : nullptr;

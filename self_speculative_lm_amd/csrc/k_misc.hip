@@ -38,18 +38,6 @@ __device__ __forceinline__ f32x4 slot_sum4(const float* P, int nslots, size_t st
   return acc;
 }
 
-// Fixed-order sum over the blockDim.x (a multiple of 64, <= 1024) threads.
-__device__ float block_sum(float v, float* red) {
-  v = wave_sum_f32(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float t = red[0];
-  for (int w = 1; w < nw; ++w) t += red[w];
-  __syncthreads();
-  return t;
-}
-
 // x[r] = E[tok[r]]; an id outside [0, n_emb) (e.g. the -1 the sampler writes
 // for a row with non-finite logits) gives a zero row instead of a stray read.
 template <typename T>
@@ -62,7 +50,9 @@ __global__ void embed_kernel(const int32_t* tok, const T* E, int n_emb, int d, f
 }
 
 // x[r] += sum of slots; y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g   (RMSNorm).
-// One 1024-thread workgroup per row, four columns per thread per pass.
+// One 1024-thread workgroup per row, four columns per thread per pass.  The
+// mean square is taken in a fixed order (16-column chunks, then one wave over
+// the chunks: sumsq4 / row_total).
 constexpr int NORM_THREADS = 1024;
 constexpr int NORM_VPT = 2;  // float4 groups per thread: d <= 1024 * 4 * 2
 // gamma is read with the row, before the reduction, and y is written with
@@ -73,11 +63,11 @@ __global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* __restr
                                                                   size_t stride, int d,
                                                                   const float* __restrict__ g, float eps,
                                                                   T* __restrict__ y) {
-  __shared__ float red[NORM_THREADS / 64];
+  __shared__ float chunk[NORM_THREADS * NORM_VPT / 4];
+  __shared__ float tot_s;
   const int r = blockIdx.x, tid = threadIdx.x;
   float* xr = x + (size_t)r * d;
   f32x4 v[NORM_VPT], gv[NORM_VPT];
-  float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NORM_VPT; ++i) {
     const int c = (tid + i * NORM_THREADS) * 4;
@@ -92,10 +82,18 @@ __global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* __restr
       }
     }
     v[i] = val;
-    ss += val[0] * val[0] + val[1] * val[1] + val[2] * val[2] + val[3] * val[3];
+    float q = sumsq4(val);
+    q += __shfl_xor(q, 1);
+    q += __shfl_xor(q, 2);
+    if ((tid & 3) == 0 && c < d) chunk[c / 16] = q;
   }
-  const float tot = block_sum(ss, red);
-  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  __syncthreads();
+  if (tid < 64) {
+    const float t = row_total(chunk, d / 16);
+    if (tid == 0) tot_s = t;
+  }
+  __syncthreads();
+  const float inv = rms_inv(tot_s, d, eps);
 #pragma unroll
   for (int i = 0; i < NORM_VPT; ++i) {
     const int c = (tid + i * NORM_THREADS) * 4;
@@ -150,19 +148,11 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
   }
 }
 
-// V element as the bf16 attention multiplies it: rounded to bf16 (the cache's
-// storage precision), then converted to fp16 with saturation at +-65504.  A
-// V cache kept in this form spares every attention workgroup that reads a
-// tile the conversion, with the same bits.
-__device__ __forceinline__ bf16_t v_cache_f16(float v) {
-  const _Float16 h = (_Float16)fminf(fmaxf(bf16_to_f32(f32_to_bf16(v)), -65504.f), 65504.f);
-  return __builtin_bit_cast(bf16_t, h);
-}
-
 // The same for head_dim 128 with vector accesses: 16 lanes per head, each
 // lane four consecutive columns of both halves (float4 slot and table loads),
 // four heads per wave.  Same arithmetic per element as rope_kv_kernel.  VF16
-// (bf16 models): V is written in the attention's fp16 form.
+// (bf16 models): V is written in the attention's fp16 form, and *vsat is set
+// when a value saturates it.
 constexpr int ROPE128_HPW = 4;                    // heads per wave
 constexpr int ROPE128_HEADS = 4 * ROPE128_HPW;    // heads per 256-thread workgroup
 template <typename T, bool VF16 = false>
@@ -170,7 +160,7 @@ __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict
                                                          int hq, int hkv, const int32_t* row_seq,
                                                          const int32_t* row_pos, const float* __restrict__ rope,
                                                          T* __restrict__ qout, T* __restrict__ kc,
-                                                         T* __restrict__ vc, int ctx, size_t css) {
+                                                         T* __restrict__ vc, int ctx, size_t css, int32_t* vsat) {
   constexpr int hd = 128, half = 64;
   const int r = blockIdx.x;
   const int h = blockIdx.y * ROPE128_HEADS + (int)(threadIdx.x >> 4);
@@ -202,16 +192,18 @@ __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict
   } else {
     const int kh = h - hq - hkv;
     const size_t o = (size_t)seq * css + (size_t)kh * hd * ctx + pos;
+    bool sat = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (VF16) {
-        vc[o + (size_t)(c + e) * ctx] = v_cache_f16(xa[e]);
-        vc[o + (size_t)(c + half + e) * ctx] = v_cache_f16(xb[e]);
+        vc[o + (size_t)(c + e) * ctx] = v_cache_f16(xa[e], sat);
+        vc[o + (size_t)(c + half + e) * ctx] = v_cache_f16(xb[e], sat);
       } else {
         Elem<T>::store(vc, o + (size_t)(c + e) * ctx, xa[e]);
         Elem<T>::store(vc, o + (size_t)(c + half + e) * ctx, xb[e]);
       }
     }
+    if (VF16 && sat && vsat) atomicOr(vsat, 1);
   }
 }
 
@@ -461,7 +453,7 @@ hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, 
 hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, size_t stride, int rows,
                              int d, const float* g, float eps, void* y, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (d > NORM_THREADS * 4 * NORM_VPT || d % 4 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  if (d > NORM_THREADS * 4 * NORM_VPT || d % 16 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
   TRI_DISPATCH(dtype,
                hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(rows), dim3(NORM_THREADS), 0, st, x, P, nslots,
                                   stride, d, g, eps, static_cast<float*>(y)),
@@ -472,14 +464,15 @@ hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, si
 
 hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, int rows, int hq, int hkv,
                           int hd, const int32_t* row_seq, const int32_t* row_pos, const float* rope,
-                          void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st, bool v_f16) {
+                          void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st, bool v_f16,
+                          int32_t* vsat) {
   if (rows <= 0) return hipSuccess;
   if (nslots > MAX_SLOTS || (v_f16 && (dtype != TRI_BF16 || hd != 128))) return hipErrorInvalidValue;
   if (v_f16) {
     const dim3 grid128(rows, (hq + 2 * hkv + ROPE128_HEADS - 1) / ROPE128_HEADS);
     hipLaunchKernelGGL((rope_kv128_kernel<bf16_t, true>), grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
                        row_seq, row_pos, rope, static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
-                       static_cast<bf16_t*>(vc), ctx, css);
+                       static_cast<bf16_t*>(vc), ctx, css, vsat);
     return hipGetLastError();
   }
   if (hd == 128) {
@@ -487,10 +480,10 @@ hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, 
     TRI_DISPATCH(dtype,
                  hipLaunchKernelGGL(rope_kv128_kernel<float>, grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
                                     row_seq, row_pos, rope, static_cast<float*>(qout), static_cast<float*>(kc),
-                                    static_cast<float*>(vc), ctx, css),
+                                    static_cast<float*>(vc), ctx, css, vsat),
                  hipLaunchKernelGGL(rope_kv128_kernel<bf16_t>, grid128, dim3(256), 0, st, P, nslots, stride, hq,
                                     hkv, row_seq, row_pos, rope, static_cast<bf16_t*>(qout),
-                                    static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, css));
+                                    static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, css, vsat));
     return hipGetLastError();
   }
   const dim3 grid(rows, (hq + 2 * hkv + ROPE_HEADS - 1) / ROPE_HEADS);

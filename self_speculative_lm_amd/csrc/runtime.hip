@@ -356,6 +356,7 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
   // rows beside it, so self-speculation, AR and mixed batches of any size
   // take the same greedy decisions; prefill chunks use the fastest slot count.
   const bool inv = logits_out != nullptr;
+  int32_t* vsat = s->dints + s->o_status + 3;
   HIPCHK(launch_embed(dt, dm.tok, n, m->embed, d.vocab + 1, D, s->x, s->st));
   int prev_slots = 0;
   size_t prev_stride = 0;
@@ -369,8 +370,9 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
       const size_t stride = (size_t)n * m->qkv_n;
       PROF(PROF_QKV, launch_gemm(dt, s->ybuf, n, D, L.qkv, m->qkv_n, m->p_qkv, s->part, stride, inv, s->st));
       // bf16 sessions keep V in the attention's fp16 form (same bits, staged without conversion)
-      HIPCHK(launch_rope_kv(dt, s->part, gemm_out_slots(dt, m->p_qkv, n, m->qkv_n, D, inv), stride, n, hq, hkv, hd, dm.seq, dm.pos, s->rope, s->qbuf, kc,
-                            vc, s->ctx, s->css, s->st, dt == TRI_BF16));
+      HIPCHK(launch_rope_kv(dt, s->part, gemm_out_slots(dt, m->p_qkv, n, m->qkv_n, D, inv), stride, n, hq, hkv, hd,
+                            dm.seq, dm.pos, s->rope, s->qbuf, kc, vc, s->ctx, s->css, s->st, dt == TRI_BF16,
+                            vsat));
     }
     {
       AttnLaunch a;
@@ -401,8 +403,8 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
       a.v_f16 = dt == TRI_BF16;
       PROF(PROF_ATTN, launch_attn(dt, a, s->st));
     }
-    int oslots = gemm_out_slots(dt, m->p_o, n, D, qd, inv);
     const size_t ostride = (size_t)n * D;
+    int oslots = gemm_out_slots(dt, m->p_o, n, D, qd, inv);
     {
       PROF(PROF_O, launch_gemm(dt, s->abuf, n, qd, L.o, D, m->p_o, s->part, ostride, inv, s->st));
     }
@@ -473,6 +475,22 @@ int d2h_ints(tri_session* s, size_t off, size_t n) {
   return TRI_OK;
 }
 
+// After a step's synchronisation: a V value that left the fp16 range of the
+// V cache (status[3], set by the RoPE/cache-write kernels; cleared here), or
+// non-finite logits in one of the step's first nslots sampling slots.  Either
+// fails the call with TRI_ENUMERIC before any sequence state moves.
+int check_status(tri_session* s, int nslots, const char* what) {
+  if (s->hints[s->o_status + 3]) {
+    s->hints[s->o_status + 3] = 0;
+    HIPCHK(hipMemsetAsync(s->dints + s->o_status + 3, 0, 4, s->st));
+    HIPCHK(hipStreamSynchronize(s->st));
+    return fail(TRI_ENUMERIC, "%s: a V value lies outside the fp16 range of the V cache (|v| > 65504)", what);
+  }
+  for (int i = 0; i < nslots; ++i)
+    if (s->hints[s->o_status + i]) return fail(TRI_ENUMERIC, "non-finite logits in %s", what);
+  return TRI_OK;
+}
+
 int check_seq(tri_session* s, int seq) {
   if (!s) return fail(TRI_EINVAL, "null session");
   if (seq < 0 || seq >= s->max_batch) return fail(TRI_EINVAL, "seq %d out of range [0,%d)", seq, s->max_batch);
@@ -498,10 +516,11 @@ int step_ar(tri_session* s, const std::vector<int>& act, int stride, int32_t* ou
   if (!rc) rc = forward(s, 0, R, s->logits);
   if (!rc) rc = sample(s, 0, R, s->logits, 0.f, 0);
   if (!rc) rc = d2h_ints(s, s->o_out_tok, R.n());
-  if (!rc) rc = d2h_ints(s, s->o_status, 1);
+  if (!rc) rc = d2h_ints(s, s->o_status, 4);
   if (rc) return rc;
   HIPCHK(hipStreamSynchronize(s->st));
-  if (s->hints[s->o_status]) return fail(TRI_ENUMERIC, "non-finite logits in AR step");
+  rc = check_status(s, 1, "AR step");
+  if (rc) return rc;
   for (size_t j = 0; j < act.size(); ++j) {
     Seq& S = s->seqs[act[j]];
     const int L = (int)S.tokens.size();
@@ -545,11 +564,12 @@ int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau
     if (!rc) rc = sample(s, 0, R, s->logits, tau, 0);
     if (!rc) rc = d2h_ints(s, s->o_out_tok, R.n());
     if (!rc) rc = d2h_ints(s, s->o_out_commit, R.n());
-    if (!rc) rc = d2h_ints(s, s->o_status, 1);
+    if (!rc) rc = d2h_ints(s, s->o_status, 4);
     if (rc) return rc;
     HIPCHK(hipMemcpyAsync(s->hconf, s->dconf, (size_t)R.n() * 4, hipMemcpyDeviceToHost, s->st));
     HIPCHK(hipStreamSynchronize(s->st));
-    if (s->hints[s->o_status]) return fail(TRI_ENUMERIC, "non-finite logits in diffusion step");
+    rc = check_status(s, 1, "diffusion step");
+    if (rc) return rc;
     for (size_t j = 0; j < na; ++j) {
       if (blk_row[j] < 0) continue;
       const std::vector<int32_t>& sched = s->seqs[act[j]].sched;
@@ -626,10 +646,11 @@ int sol_parallel(tri_session* s, const std::vector<int>& act, int B, const std::
     if (!rc) rc = forward(s, 0, R, s->logits);
     if (!rc) rc = sample(s, 0, R, s->logits, 1.f, 0);
     if (!rc) rc = d2h_ints(s, s->o_out_tok, R.n());
-    if (!rc) rc = d2h_ints(s, s->o_status, 1);
+    if (!rc) rc = d2h_ints(s, s->o_status, 4);
     if (rc) return rc;
     HIPCHK(hipStreamSynchronize(s->st));
-    if (s->hints[s->o_status]) return fail(TRI_ENUMERIC, "non-finite logits in the speed-of-light pass");
+    rc = check_status(s, 1, "the speed-of-light pass");
+    if (rc) return rc;
     for (size_t j = 0; j < na; ++j) {
       if (blk_row[j] < 0) continue;
       std::vector<int> now;
@@ -755,11 +776,11 @@ int step_round(tri_session* s, const std::vector<int>& act, const std::vector<ch
   rc = d2h_ints(s, s->o_accept, na);
   if (!rc) rc = d2h_ints(s, s->o_committed, na * (k + 1));
   if (!rc && any_ar) rc = d2h_ints(s, s->o_ars, na * (k + 1));
-  if (!rc) rc = d2h_ints(s, s->o_status, 2);
+  if (!rc) rc = d2h_ints(s, s->o_status, 4);
   if (rc) return rc;
   HIPCHK(hipStreamSynchronize(s->st));
-  if (s->hints[s->o_status] || s->hints[s->o_status + 1])
-    return fail(TRI_ENUMERIC, "non-finite logits in a self-speculation / mixed round");
+  rc = check_status(s, 2, "a self-speculation / mixed round");
+  if (rc) return rc;
   for (size_t j = 0; j < na; ++j) {
     Seq& S = s->seqs[act[j]];
     const int L = (int)S.tokens.size();
@@ -931,13 +952,13 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   for (int l = 0; l < d.n_layers; ++l) {
     const ModelLayout::L& L = ML.layers[l];
     WSeg qkv[3] = {{weights[w], qd}, {weights[w + 1], kd}, {weights[w + 2], kd}};
-    HIPCHK(launch_pack(dt, qkv, 3, qd + 2 * kd, d.d_model, P.qkv, base + L.qkv, false, st));
+    HIPCHK(launch_pack(dt, qkv, 3, qd + 2 * kd, d.d_model, P.qkv, base + L.qkv, PACK_PLAIN, st));
     WSeg o = {weights[w + 3], d.d_model};
-    HIPCHK(launch_pack(dt, &o, 1, d.d_model, qd, P.o, base + L.o, false, st));
+    HIPCHK(launch_pack(dt, &o, 1, d.d_model, qd, P.o, base + L.o, PACK_PLAIN, st));
     WSeg gu[2] = {{weights[w + 4], d.d_ffn}, {weights[w + 5], d.d_ffn}};
-    HIPCHK(launch_pack(dt, gu, 2, 2 * d.d_ffn, d.d_model, P.gu, base + L.gu, true, st));
+    HIPCHK(launch_pack(dt, gu, 2, 2 * d.d_ffn, d.d_model, P.gu, base + L.gu, PACK_GATEUP, st));
     WSeg dn = {weights[w + 6], d.d_model};
-    HIPCHK(launch_pack(dt, &dn, 1, d.d_model, d.d_ffn, P.down, base + L.down, false, st));
+    HIPCHK(launch_pack(dt, &dn, 1, d.d_model, d.d_ffn, P.down, base + L.down, PACK_PLAIN, st));
     HIPCHK(hipMemcpyAsync(base + L.n1, weights[w + 7], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(hipMemcpyAsync(base + L.n2, weights[w + 8], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
     w += 9;
@@ -945,14 +966,14 @@ int tri_model_create(const tri_model_desc* desc, const void* const* weights, int
   HIPCHK(hipMemcpyAsync(base + ML.final_norm, weights[w++], (size_t)d.d_model * 4, hipMemcpyDeviceToDevice, st));
   {
     WSeg lm = {weights[w++], d.vocab};
-    HIPCHK(launch_pack(dt, &lm, 1, d.vocab, d.d_model, P.lm, base + ML.lm_head, false, st));
+    HIPCHK(launch_pack(dt, &lm, 1, d.vocab, d.d_model, P.lm, base + ML.lm_head, PACK_PLAIN, st));
   }
   if (d.lora_rank > 0)
     for (int l = 0; l < d.n_layers; ++l) {
       WSeg a = {weights[w++], d.lora_rank};
-      HIPCHK(launch_pack(dt, &a, 1, d.lora_rank, qd, P.la, base + ML.layers[l].la, false, st));
+      HIPCHK(launch_pack(dt, &a, 1, d.lora_rank, qd, P.la, base + ML.layers[l].la, PACK_PLAIN, st));
       WSeg b = {weights[w++], d.d_model};
-      HIPCHK(launch_pack(dt, &b, 1, d.d_model, d.lora_rank, P.lb, base + ML.layers[l].lb, false, st));
+      HIPCHK(launch_pack(dt, &b, 1, d.d_model, d.lora_rank, P.lb, base + ML.layers[l].lb, PACK_PLAIN, st));
     }
   HIPCHK(hipStreamSynchronize(st));
   tri_model* m = new tri_model();
@@ -1132,7 +1153,17 @@ int tri_prefill(tri_session* s, int seq, const int32_t* tokens, int n) {
       return rc;
     }
   }
+  rc = d2h_ints(s, s->o_status, 4);
+  if (rc) {
+    S.active = false;
+    return rc;
+  }
   HIPCHK(hipStreamSynchronize(s->st));
+  rc = check_status(s, 0, "prefill");
+  if (rc) {
+    S.active = false;
+    return rc;
+  }
   S.kv_len = n - 1;
   S.written_hi = n - 1;
   return TRI_OK;
@@ -1387,9 +1418,12 @@ int tri_forward(tri_session* s, int n_rows, const int32_t* row_seq, const int32_
   if (!rc) rc = forward(s, 0, R, lg);
   if (!rc) rc = sample(s, 0, R, lg, 0.f, 0);
   if (!rc) rc = d2h_ints(s, s->o_out_tok, n_rows);
+  if (!rc) rc = d2h_ints(s, s->o_status, 4);
   if (rc) return rc;
   HIPCHK(hipMemcpyAsync(s->hconf, s->dconf, (size_t)n_rows * 4, hipMemcpyDeviceToHost, s->st));
   HIPCHK(hipStreamSynchronize(s->st));
+  rc = check_status(s, 0, "teacher-forced forward");
+  if (rc) return rc;
   if (out_tok) memcpy(out_tok, s->hints + s->o_out_tok, (size_t)n_rows * 4);
   if (out_conf) memcpy(out_conf, s->hconf, (size_t)n_rows * 4);
   return TRI_OK;
@@ -1514,6 +1548,8 @@ int block_causal_attn(const void* q, const void* k_cache, const void* v_cache, i
   if (rows < 0 || n_seq <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_rows_per_seq < 0 || max_hi < 0)
     return fail(TRI_EINVAL, "bad shape");
   if (ctx <= 0 || ctx % 64 || max_hi > ctx) return fail(TRI_EINVAL, "ctx must be a positive multiple of 64 >= max_hi");
+  const bool v16 = dtype == TRI_BF16_V16;
+  if (v16) dtype = TRI_BF16;
   if (dtype == TRI_BF16 ? hd != 128 : (dtype == TRI_F32 ? (hd > 128 || hd <= 0) : true))
     return fail(TRI_EINVAL, "unsupported dtype/head_dim");
   if (!(scale > 0)) return fail(TRI_EINVAL, "scale must be positive");
@@ -1540,6 +1576,7 @@ int block_causal_attn(const void* q, const void* k_cache, const void* v_cache, i
   a.kv_split = kv_split;
   a.out = out;
   a.part = static_cast<float*>(ws);
+  a.v_f16 = v16;
   HIPCHK(launch_attn(dtype, a, static_cast<hipStream_t>(stream)));
   return TRI_OK;
 }

@@ -75,6 +75,44 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
   }));
 }
 
+// V element as the bf16 attention multiplies it: rounded to bf16 (the cache's
+// storage precision), then converted to fp16 with saturation at +-65504.  A
+// V cache kept in this form spares every attention workgroup that reads a
+// tile the conversion, with the same bits.  `sat` is set when the bf16 value
+// lies outside the fp16 range (the saturation changed it).
+__device__ __forceinline__ bf16_t v_cache_f16(float v, bool& sat) {
+  const float b = bf16_to_f32(f32_to_bf16(v));
+  sat = sat || fabsf(b) > 65504.f;
+  const _Float16 h = (_Float16)fminf(fmaxf(b, -65504.f), 65504.f);
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+// RMSNorm statistic in one fixed order.  The row is cut into chunks of 16
+// columns: a chunk's sum of squares is ((q0 + q1) + (q2 + q3)) over its four
+// groups of four consecutive columns, each group fmaf(v3, v3, fmaf(v2, v2,
+// fmaf(v1, v1, v0 * v0))).  The row total is then reduced by one wave: lane
+// i adds chunks i, i + 64, ..., i + 448 in that order (zero past the row's
+// chunks, so at most 512 chunks: d <= 8192), and the lanes are summed by
+// wave_sum_f32.
+constexpr int ROW_CHUNK_STRIDES = 8;
+__device__ __forceinline__ float sumsq4(f32x4 v) {
+  return fmaf(v[3], v[3], fmaf(v[2], v[2], fmaf(v[1], v[1], v[0] * v[0])));
+}
+__device__ __forceinline__ float row_total(const float* part, int nch) {
+  const int lane = threadIdx.x & 63;
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < ROW_CHUNK_STRIDES; ++j) {
+    const int i = lane + 64 * j;
+    const float v = i < nch ? part[i] : 0.f;
+    acc = j == 0 ? v : acc + v;
+  }
+  return wave_sum_f32(acc);
+}
+__device__ __forceinline__ float rms_inv(float total, int d, float eps) {
+  return 1.0f / sqrtf(total / (float)d + eps);
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  All are asynchronous.
 
@@ -96,8 +134,11 @@ GemmPlan gemm_plan(int N, int K, int dtype, bool unsplit = false);
 // rows padded to 128, K padded to S*Ks; float32: row-major) and the packing
 // launch (segments concatenated by rows).
 size_t gemm_packed_bytes(const GemmPlan& p, int N, int K, int dtype);
+// Packed row order: PACK_PLAIN keeps the segments' rows; PACK_GATEUP
+// interleaves two equal segments in groups of 16 rows (gate/up pairs).
+enum { PACK_PLAIN = 0, PACK_GATEUP = 1 };
 hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, const GemmPlan& p, void* dst,
-                       bool interleave, hipStream_t st);
+                       int order, hipStream_t st);
 // Y = X W^T with W packed by launch_pack.
 // Output slots a launch_gemm of M rows writes (the consumer adds them in slot
 // order): the plan's S on the decode kernel, fewer on the large-M kernel
@@ -137,10 +178,11 @@ hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, 
                         float* x, hipStream_t st);
 hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, size_t slot_stride,
                              int rows, int d, const float* g, float eps, void* y, hipStream_t st);
+// vsat: set to 1 when a V value saturates its fp16 form (v_f16).
 hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
                           int hq, int hkv, int hd, const int32_t* row_seq, const int32_t* row_pos,
                           const float* rope, void* qout, void* kc, void* vc, int ctx,
-                          size_t cache_seq_stride, hipStream_t st, bool v_f16 = false);
+                          size_t cache_seq_stride, hipStream_t st, bool v_f16 = false, int32_t* vsat = nullptr);
 hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
                          int ffn, void* h, hipStream_t st);
 hipError_t launch_lora_mid(int dtype, const float* P, int nslots, size_t slot_stride, int rows,

@@ -54,13 +54,25 @@ def get(shape):
     return _cache[shape.name]
 
 
-def check_teacher_forced(shape, oms, sess, max_ctx, prompts):
+def check_teacher_forced(shape, oms, sess, max_ctx, prompts, label=""):
+    """Replay every traced GPU forward through the float64 oracle and through
+    the float32-projection oracle (the floor), on the GPU's own rows.
+
+    Reading R21 (logit bound at full width): max |GPU - oracle| <=
+    max(2e-2 x lm_head scale, 2 x the floor's max) and median <= 1.5 x the
+    floor's median.  Reading R22 (greedy decisions): a GPU argmax may differ
+    from the oracle's only where the oracle's top-2 margin is <= 2 x the
+    forward's max error, and on at most max(10% of the decisions, 2 x the
+    floor's own flips + 1) rows -- the float32-projection oracle flips
+    decisions too, more of them the deeper the model.  Flips at margins below
+    1e-3 (the plain near-tie rule) and flips allowed only by the wider rule are
+    counted separately and printed with the errors."""
     om, om32 = oms
     tr = sess.trace()
     ref = replay(shape, om, tr, max_ctx, prompts=prompts)
     ref32 = replay(shape, om32, tr, max_ctx, prompts=prompts)
     errs, floors = [], []
-    decisions = flips = 0
+    decisions = flips_tie = flips_wide = floor_flips = 0
     for r, r32, t in zip(ref, ref32, tr):
         if r is None:
             continue
@@ -70,14 +82,24 @@ def check_teacher_forced(shape, oms, sess, max_ctx, prompts):
         e = float(d.max())
         for i in range(len(r)):
             decisions += 1
+            if vocab_reduce(r32[i])[0] != vocab_reduce(r[i])[0]:
+                floor_flips += 1
             if int(np.argmax(t["logits"][i])) != vocab_reduce(r[i])[0]:
-                assert top2_margin(r[i]) <= 2 * e, (i, top2_margin(r[i]), e)
-                flips += 1
+                m = top2_margin(r[i])
+                assert m <= 2 * e, (i, m, e)
+                if m < 1e-3:
+                    flips_tie += 1
+                else:
+                    flips_wide += 1
     err, floor = np.concatenate(errs), np.concatenate(floors)
     tol_max = max(TOL_BF16 * shape.lm_head_scale, 2.0 * float(floor.max()))
+    print(f"[parity {label or shape.name}] forwards {sum(r is not None for r in ref)}, max |err| "
+          f"{float(err.max()):.4f} (floor {float(floor.max()):.4f}, bound {tol_max:.4f}), median "
+          f"{float(np.median(err)):.5f} (floor {float(np.median(floor)):.5f}), decisions {decisions}, flips "
+          f"at margin < 1e-3: {flips_tie}, wider: {flips_wide}, the floor's own flips: {floor_flips}", flush=True)
     assert float(err.max()) <= tol_max, (float(err.max()), float(floor.max()))
     assert float(np.median(err)) <= 1.5 * float(np.median(floor)), (float(np.median(err)), float(np.median(floor)))
-    assert flips <= 0.1 * max(decisions, 1)
+    assert flips_tie + flips_wide <= max(0.1 * decisions, 2 * floor_flips + 1), (flips_tie, flips_wide, floor_flips)
     return float(err.max()), float(floor.max())
 
 
@@ -285,3 +307,64 @@ def test_14b_full_depth_lora_selfspec_equals_ar_behind_a_16k_prefix():
         got = sess.state(0)[0]
         assert got == ref[: len(got)], a_star
         sess.set_draft_override(0, None, -1)
+
+
+def _full_model(shape):
+    """Seeded weights of a whole model: device copy for the library (uploaded
+    one tensor at a time) and the float32 host arrays for the oracle."""
+    import torch
+    _cache.clear()
+    arrays = seeded.gen_weights(shape)
+    tens = {}
+    for name, a in arrays.items():
+        t = torch.from_numpy(a)
+        tens[name] = (t.to(torch.float32) if name.endswith("norm") else t.to(torch.bfloat16)).to("cuda")
+        del t
+    model = make_model(shape, tens)
+    del tens
+    torch.cuda.empty_cache()
+    om = OracleModel(shape, arrays, batched_linear=True, keep_float32=True)
+    om32 = OracleModel(shape, arrays, batched_linear=True, keep_float32=True, proj_dtype=np.float32)
+    return model, om, om32
+
+
+@pytest.mark.timeout(900)
+def test_8b_full_depth_round_teacher_forced_against_the_oracle():
+    """One self-speculation round of the whole 36-layer 8B-class model in the
+    benchmark's launch configuration (512-token prompt prefilled as one
+    511-row chunk, draft block 32, batch 1, the benchmark's session split):
+    the draft (33 rows) and verify (32 rows) forwards are traced and replayed
+    through the float64 oracle on top of the oracle's prefill of the same
+    prompt (readings R21, R22)."""
+    import self_speculative_lm_amd as tm
+    shape = seeded.MODEL_8B
+    model, om, om32 = _full_model(shape)
+    prompt = seeded.prompt(512, shape.vocab)
+    max_ctx = 512 + 33 * 35 + 64          # the benchmark's session size (128-key attention splits)
+    sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=512)
+    sess.prefill(0, prompt)
+    sess.set_trace(True)
+    _, st = sess.decode_step(tm.TRI_SELFSPEC, 32)
+    assert st[0][1] == 2
+    check_teacher_forced(shape, (om, om32), sess, max_ctx, [prompt], label="8B 36 layers, bench round")
+
+
+@pytest.mark.timeout(900)
+def test_14b_full_depth_lora_round_teacher_forced_against_the_oracle():
+    """One self-speculation round of the whole 40-layer 14B-class model with the
+    rank-128 draft LoRA, replayed through the float64 oracle.  The prefix is
+    128 tokens (the oracle's prefill of the 16384-token prefix does not fit the
+    test's CPU time); the long-prefix attention of that configuration is
+    compared with the oracle directly by the fp16-V kernel tests."""
+    import self_speculative_lm_amd as tm
+    shape = seeded.MODEL_14B
+    model, om, om32 = _full_model(shape)
+    prompt = seeded.prompt(128, shape.vocab, stream=401)
+    max_ctx = 128 + 2 * 33 + 64
+    sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=512)
+    sess.prefill(0, prompt)
+    sess.set_lora(True)
+    sess.set_trace(True)
+    _, st = sess.decode_step(tm.TRI_SELFSPEC, 32)
+    assert st[0][1] == 2
+    check_teacher_forced(shape, (om, om32), sess, max_ctx, [prompt], label="14B 40 layers + LoRA round")

@@ -19,7 +19,11 @@ ATT_TOL_BF16 = 2.5e-2
 ATT_TOL_F32 = 2e-5
 
 
-def _attn_case(prefixes, nrows, hq, hkv, hd, bf16, causal=False, kv_split=0, seed=3, sample=None):
+def _attn_case(prefixes, nrows, hq, hkv, hd, bf16, causal=False, kv_split=0, seed=3, sample=None, vf16=False,
+               v_scale=1.0, return_max=False):
+    """Max |GPU - oracle| over the sampled rows.  vf16: the V cache is passed in
+    the session's fp16 form (TRI_BF16_V16) of the same bf16 values; v_scale
+    (a power of two) scales V exactly."""
     import torch
     import self_speculative_lm_amd as tm
     b = len(prefixes)
@@ -27,15 +31,17 @@ def _attn_case(prefixes, nrows, hq, hkv, hd, bf16, causal=False, kv_split=0, see
     ctx = (maxlen + 63) // 64 * 64
     R = max(nrows)
     q, k, v = seeded.attention_operands(R, max(prefixes), hq, hkv, hd, batch=b, bf16=bf16, seed=seed)
+    if v_scale != 1.0:
+        v = v * np.float32(v_scale)
     # k, v: [b, Pmax + R, hkv, hd]; sequence s uses positions [0, P_s + n_s)
     tdt = torch.bfloat16 if bf16 else torch.float32
     kc = torch.zeros((b, hkv, ctx, hd), dtype=tdt)
-    vc = torch.zeros((b, hkv, hd, ctx), dtype=tdt)
+    vc = torch.zeros((b, hkv, hd, ctx), dtype=torch.float16 if vf16 else tdt)
     qs, his, starts = [], [], [0]
     for s in range(b):
         L = prefixes[s] + nrows[s]
         kc[s, :, :L] = torch.from_numpy(k[s, :L]).permute(1, 0, 2).to(tdt)
-        vc[s, :, :, :L] = torch.from_numpy(v[s, :L]).permute(1, 2, 0).to(tdt)
+        vc[s, :, :, :L] = torch.from_numpy(v[s, :L]).permute(1, 2, 0).to(tdt).to(vc.dtype)
         qs.append(q[s, : nrows[s]])
         for i in range(nrows[s]):
             his.append(prefixes[s] + i + 1 if causal else L)
@@ -51,14 +57,17 @@ def _attn_case(prefixes, nrows, hq, hkv, hd, bf16, causal=False, kv_split=0, see
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     rows = list(range(len(his))) if sample is None else sample
-    err = 0.0
+    err = vmax = 0.0
+    cache = {}
     for r in rows:
         s = int(np.searchsorted(starts, r, side="right") - 1)
-        K = k[s].astype(np.float64)
-        V = v[s].astype(np.float64)
+        if s not in cache:
+            cache = {s: (k[s].astype(np.float64), v[s].astype(np.float64))}
+        K, V = cache[s]
         ref = attend(qn[r].astype(np.float64), K, V, his[r], hq // hkv)
         err = max(err, float(np.abs(ref - got[r]).max()))
-    return err
+        vmax = max(vmax, float(np.abs(ref).max()))
+    return (err, vmax) if return_max else err
 
 
 @pytest.mark.parametrize("prefixes,nrows,causal,kv_split", [
@@ -89,6 +98,38 @@ def test_block_causal_attn_bf16_group5(prefixes, nrows, kv_split):
     n = sum(nrows)
     sample = sorted(set(rng.integers(0, n, 8).tolist() + [0, n - 1]))
     assert _attn_case(prefixes, nrows, 40, 8, 128, True, False, kv_split, sample=sample) <= ATT_TOL_BF16
+
+
+@pytest.mark.parametrize("prefixes,nrows,hq,causal,kv_split", [
+    ([16384], [33], 40, False, 1024),           # the 14B-class draft forward behind a 16K prefix
+    ([16384], [32], 40, True, 1024),            # its verify forward (causal rows)
+    ([32768], [33], 40, False, 1024),
+    ([32768] * 8, [32] * 8, 32, False, 0),      # eight sequences of 32K keys
+])
+def test_block_causal_attn_fp16_v_cache_matches_oracle(prefixes, nrows, hq, causal, kv_split):
+    """The V cache form a bf16 session keeps (fp16 bits of the bf16 values),
+    at the long-prefix launch shapes the sessions use: 1024-key splits and two
+    query tiles per slot (a 33-row block of 5-head groups is 165 query
+    vectors)."""
+    rng = np.random.default_rng(sum(prefixes) + len(prefixes))
+    n = sum(nrows)
+    sample = sorted(set(rng.integers(0, n, 6).tolist() + [0, n - 1]))
+    err = _attn_case(prefixes, nrows, hq, 8, 128, True, causal, kv_split, sample=sample, vf16=True)
+    print(f"fp16-V attention {prefixes[0]} keys x {len(prefixes)}, {hq}q: max |err| {err:.3e}")
+    assert err <= ATT_TOL_BF16, err
+
+
+def test_block_causal_attn_fp16_v_cache_subnormal_values():
+    """V values below fp16's normal range (2^-20 * N(0,1), about 1e-6) become
+    fp16 subnormals in the cache: each loses at most half a subnormal step,
+    2^-25, so a convex combination of them moves by at most 2^-25.  With the
+    bf16 output rounding (2^-9 of the output) and the fp16 P (2^-12 of the
+    values) the bound is 2^-25 + 2^-8 * max|out| + 2^-11 * max|v|."""
+    scale = 2.0 ** -20
+    err, omax = _attn_case([700], [33], 32, 8, 128, True, False, 256, vf16=True, v_scale=scale, return_max=True)
+    bound = 2.0 ** -25 + 2.0 ** -8 * omax + 2.0 ** -11 * 6 * scale
+    print(f"subnormal V: max |err| {err:.3e}, bound {bound:.3e}")
+    assert err <= bound, (err, bound)
 
 
 @pytest.mark.parametrize("prefix,nrows,kv_split", [(600, 33, 256), (5000, 33, 512), (130, 40, 64), (6000, 33, 4096),

@@ -456,3 +456,33 @@ def test_tiny_scheduled_commit_rate_matches_oracle():
     assert toks[0][:8].tolist() == o.diffusion_block(8, 0.9)
     with pytest.raises(tm.TriError):
         sess.set_commit_schedule(0, [2, 0])
+
+
+def test_fp16_v_cache_out_of_range_fails_the_step():
+    """A bf16 session keeps V in fp16 form (exact for |v| <= 65504).  A value
+    outside that range is not saturated silently: the prefill or step that
+    writes it fails with TRI_ENUMERIC and leaves the sequence as it was
+    (reading R23).  Wv scaled by 2^18 (bf16-exact) puts |v| near 1e5."""
+    import torch
+    import self_speculative_lm_amd as tm
+    shape = seeded.SMALL_BF16
+    arrays, tens, _, _ = get(shape)
+    big = dict(tens)
+    big["layers.1.wv"] = (tens["layers.1.wv"].float() * 2.0 ** 18).to(torch.bfloat16)
+    model = make_model(shape, big)
+    sess = tm.Session(model, max_batch=1, max_ctx=64, max_rows=64)
+    with pytest.raises(tm.TriError) as e:
+        sess.prefill(0, seeded.prompt(16, shape.vocab))
+    assert e.value.code == tm._lib.TRI_ENUMERIC and "fp16" in str(e.value)
+    # a one-token prompt writes no V; the AR step's pending row does
+    sess.prefill(0, seeded.prompt(1, shape.vocab))
+    before = sess.state(0)
+    with pytest.raises(tm.TriError) as e:
+        sess.decode_step(tm.TRI_AR, 1)
+    assert e.value.code == tm._lib.TRI_ENUMERIC
+    after = sess.state(0)
+    assert list(after[0]) == list(before[0]) and after[1] == before[1]
+    # the flag was cleared: the same session still runs a model in range
+    ok = tm.Session(get(shape)[2], max_batch=1, max_ctx=64, max_rows=64)
+    ok.prefill(0, seeded.prompt(16, shape.vocab))
+    ok.decode_step(tm.TRI_AR, 1)

@@ -26,13 +26,16 @@ textbook forward, RoPE closed forms, a brute-force acceptance loop, the
 losslessness of self-speculation against greedy AR (also in mixed AR /
 self-speculation steps), KV-rollback equality with an AR cache, the diffusion
 threshold edge cases, closed forms of the mode choice by concurrency, and
-closed forms plus a textbook replay of the speed-of-light analysis.  No function here is
-"parity unpinned" except the diffusion trajectory itself for thresholds
-strictly inside (0, 1), for which the pages print no worked example.
+closed forms plus a textbook replay of the speed-of-light analysis, and the
+quadratic self-speculation round against a dense-mask textbook forward of all
+its rows plus its losslessness.  Parity unpinned by the pages: the diffusion
+trajectory itself for thresholds strictly inside (0, 1), for which the pages
+print no worked example, and the quadratic self-speculation layout (reading
+R24), which the pages name but do not describe; only its invariants pin it.
 """
 from .numerics import round_bf16  # noqa: F401
 from .model import OracleModel, Row, KVCache, forward  # noqa: F401
 from .sampler import vocab_reduce, commit_set, accept_length  # noqa: F401
-from .decode import OracleSession, MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC  # noqa: F401
+from .decode import OracleSession, MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC, MODE_QUADSPEC  # noqa: F401
 from .policy import choose_modes, forward_ms, step_rate  # noqa: F401
 from .sol import sol_block  # noqa: F401

@@ -16,6 +16,12 @@ clean causal rows, optionally followed by a block of rows at [L, L + nb).
   gives g1..gk; the longest matching prefix a is accepted and g0..ga committed
   (1..k+1 tokens), the K/V of the k - a rejected rows rolled back.
 
+* Quadratic self-speculation ([Notes §8.1]; [Blog], performance highlights;
+  reading R24): one forward per round verifies the drafts carried from the
+  previous round and, for every possible accept length, drafts the next
+  block: (k + 1) blocks of k + 1 [MASK] rows, so the forward has
+  1 + k + (k + 1)^2 rows.
+
 Every step counts its executed forwards; TPF = committed tokens / forwards,
 the draft and verify forwards counted separately (reading R17).
 """
@@ -29,7 +35,7 @@ import numpy as np
 from .model import KVCache, OracleModel, Row, forward
 from .sampler import accept_length, commit_set, vocab_reduce
 
-MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC = 0, 1, 2
+MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC, MODE_QUADSPEC = 0, 1, 2, 3
 
 
 @dataclasses.dataclass
@@ -52,6 +58,9 @@ class OracleSession:
         self.keep_logits = keep_logits
         self.prefill_chunk = prefill_chunk
         self.records: List[ForwardRecord] = []
+        # quadratic self-speculation: drafts for positions L .. L+k-1 carried
+        # from the previous round (None: the next round starts without drafts)
+        self.qdrafts: Optional[List[int]] = None
 
     # -- basic pieces ---------------------------------------------------
     @property
@@ -72,6 +81,7 @@ class OracleSession:
     def prefill(self, prompt) -> None:
         """Run x[0..P-1) causally into the cache; x[P-1] stays pending (R15).
         Not counted as decode forwards."""
+        self.qdrafts = None
         toks = [int(t) for t in prompt]
         if not toks:
             raise ValueError("empty prompt")
@@ -92,9 +102,11 @@ class OracleSession:
         if n < 0 or n > self.kv_len:
             raise ValueError("bad rollback")
         self.kv_len -= n
+        self.qdrafts = None
 
     # -- the three modes -------------------------------------------------
     def ar_step(self) -> List[int]:
+        self.qdrafts = None
         rows = self.clean_rows()
         logits = self.run(rows)
         g, _ = vocab_reduce(logits[-1])
@@ -104,6 +116,7 @@ class OracleSession:
         return [g]
 
     def diffusion_block(self, block: int, threshold: float) -> List[int]:
+        self.qdrafts = None
         mask = self.model.shape.mask_id
         L = self.L
         y = [mask] * block
@@ -137,6 +150,7 @@ class OracleSession:
         those of the threshold rule, only the number committed is fixed."""
         if not counts or min(counts) < 1:
             raise ValueError("commit counts must be >= 1")
+        self.qdrafts = None
         mask = self.model.shape.mask_id
         L = self.L
         y = [mask] * block
@@ -183,12 +197,65 @@ class OracleSession:
         return [vocab_reduce(logits[i])[0] for i in range(len(d))]
 
     def selfspec_round(self, k: int, lora: bool = False) -> List[int]:
+        self.qdrafts = None
         g0, d = self.draft(k, lora)
         g = [g0] + self.verify(d)
         a = accept_length(d, g)
         L = self.L
         self.tokens.extend(g[: a + 1])
         self.kv_len = L + a          # append the k verify rows, roll back k - a
+        self.rounds += 1
+        self.accepts.append(a)
+        return g[: a + 1]
+
+    def quad_rows(self, k: int):
+        """The rows of one quadratic round (reading R24): the clean rows (the
+        pending tokens, then the carried drafts at L .. L+len(drafts)-1, hi =
+        pos + 1) and, for b = 0 .. len(drafts), block b: k + 1 [MASK] rows at
+        L+b .. L+b+k (LoRA rows) that see the clean stream [0, L+b) and each
+        other."""
+        mask = self.model.shape.mask_id
+        L = self.L
+        drafts = self.qdrafts or []
+        clean = self.clean_rows() + [Row(t, L + i, L + i + 1) for i, t in enumerate(drafts)]
+        blocks = [[Row(mask, L + b + j, L + b + k + 1, lora=True) for j in range(k + 1)]
+                  for b in range(len(drafts) + 1)]
+        return clean, blocks
+
+    def quad_forward(self, clean: List[Row], blocks: List[List[Row]], lora: bool = False):
+        """One forward over the rows of quad_rows: the clean rows run into the
+        cache; each block runs on a copy of that cache, where its own K/V take
+        positions L+b .. L+b+k, so a block sees [0, L+b) of the clean stream and
+        itself, never the drafts past L+b or another block.  Returns the clean
+        rows' logits and each block's logits; counts one forward."""
+        logits = forward(self.model, self.cache, clean)
+        blk = [forward(self.model, self.cache.copy(), rows, lora_enabled=lora) for rows in blocks]
+        self.forwards += 1
+        self.records.append(ForwardRecord(clean + [r for rows in blocks for r in rows], lora,
+                                          np.concatenate([logits] + blk) if self.keep_logits else None))
+        return logits, blk
+
+    def quad_round(self, k: int, lora: bool = False) -> List[int]:
+        """One round of quadratic self-speculation (reading R24).  The AR
+        pathway verifies the carried drafts d_0..d_{n-1} (n = k, or 0 on the
+        first round and after any other step): g_0 is the greedy token of the
+        last pending row, g_{i+1} that of draft row i.  a = accept_length(d, g);
+        g_0..g_a are committed (1..n+1 tokens); the K/V of the pending rows and
+        of d_0..d_{a-1} stay, the rest is rolled back; g_a becomes the pending
+        token.  The next drafts are block a's greedy tokens at L+a+1 .. L+a+k
+        (its row at L+a, the position g_a now holds, is not used)."""
+        if not 1 <= k <= 63:
+            raise ValueError("quadratic self-speculation needs 1 <= k <= 63")
+        L = self.L
+        c = L - self.kv_len
+        drafts = self.qdrafts or []
+        clean, blocks = self.quad_rows(k)
+        logits, blk = self.quad_forward(clean, blocks, lora)
+        g = [vocab_reduce(logits[c - 1 + i])[0] for i in range(len(drafts) + 1)]
+        a = accept_length(drafts, g)
+        self.tokens.extend(g[: a + 1])
+        self.kv_len = L + a
+        self.qdrafts = [vocab_reduce(blk[a][1 + i])[0] for i in range(k)]
         self.rounds += 1
         self.accepts.append(a)
         return g[: a + 1]
@@ -215,6 +282,8 @@ class OracleSession:
                 out += self.diffusion_block(block, threshold)
             elif mode == MODE_SELFSPEC:
                 out += self.selfspec_round(block, lora)
+            elif mode == MODE_QUADSPEC:
+                out += self.quad_round(block, lora)
             else:
                 raise ValueError(f"bad mode {mode}")
         return out[:n_new]

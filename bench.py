@@ -125,54 +125,90 @@ def cpu_baseline(shape, prefix, k, tpr, repeats=5):
             "seconds_measured": round(total, 2)}
 
 
+def gpu_clocks():
+    """Current shader and memory clocks as rocm-smi reports them (None when the
+    tool is missing or prints no clocks)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20).stdout
+        data = json.loads(out)
+    except Exception:  # noqa: BLE001 - the clocks are context, never required
+        return None
+    card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
+    keep = {k: v for k, v in card.items() if "clock" in k.lower() and ("sclk" in k.lower() or "mclk" in k.lower())}
+    return keep or None
+
+
 def attention_alone(args):
     """Block-causal attention alone through the C-ABI, at the attention-only
-    shapes (32 q / 8 kv heads x 128, a 32-row block attending bidirectionally
-    to itself and causally to the prefix): one JSON line per (prefix, batch)
-    with the launch time (HIP events on the launch stream, inputs resident)
-    against the HBM roofline of the K/V bytes it must read."""
+    shapes (32 q / 8 kv heads x 128, a 32-row block per sequence): one JSON
+    line per (prefix, batch, variant) with the launch time against the HBM
+    roofline of the K/V bytes it must read.
+
+    Variants: block rows (every row sees the whole prefix and block), causal
+    rows (row i sees prefix + i + 1 keys: the verify shape), and block rows
+    with the V cache in the fp16 form the sessions keep.  Timing protocol:
+    buffer sets are rotated (at least four, and enough that the sets cover
+    1 GiB, so the 256 MB Infinity Cache cannot serve a set's K/V from a
+    previous launch); 20 batches of back-to-back launches over all sets, each
+    batch timed with HIP events on the launch stream; median, p10 and p90 of
+    the per-launch time over the batches; clocks before and after."""
+    import numpy as np
     import torch
     import self_speculative_lm_amd as tm
     dev = "cuda:0"
     torch.cuda.set_device(0)
     hq, hkv, hd, nb = 32, 8, 128, 32
     g = torch.Generator(device=dev).manual_seed(3)
+    clocks0 = gpu_clocks()
     for P in (512, 2048, 8192, 32768):
         for b in (1, 8):
             L = P + nb
             ctx = (L + 63) // 64 * 64
-            kc = torch.randn((b, hkv, ctx, hd), generator=g, device=dev).to(torch.bfloat16)
-            vc = torch.randn((b, hkv, hd, ctx), generator=g, device=dev).to(torch.bfloat16)
+            set_bytes = b * hkv * ctx * hd * 2 * 2
+            nsets = int(min(256, max(4, math.ceil((1 << 30) / set_bytes))))
+            kcs = torch.randn((nsets, b, hkv, ctx, hd), generator=g, device=dev).to(torch.bfloat16)
+            vcs = torch.randn((nsets, b, hkv, hd, ctx), generator=g, device=dev).to(torch.bfloat16)
+            vcs16 = vcs.to(torch.float16)
             q = torch.randn((b * nb, hq, hd), generator=g, device=dev).to(torch.bfloat16)
             out = torch.empty_like(q)
             ss = torch.arange(0, b * nb + 1, nb, dtype=torch.int32, device=dev)
-            hi = torch.full((b * nb,), L, dtype=torch.int32, device=dev)
+            block_hi = torch.full((b * nb,), L, dtype=torch.int32, device=dev)
+            causal_hi = (P + 1 + torch.arange(nb, dtype=torch.int32, device=dev)).repeat(b)
             ws = torch.empty(tm.block_causal_attn_ws_bytes(b * nb, hq, hd, L), dtype=torch.uint8, device=dev)
-
-            def run():
-                tm.block_causal_attn(q, kc, vc, ss, hi, out, 1.0 / math.sqrt(hd), max_rows_per_seq=nb, max_hi=L,
-                                     ws=ws)
-            for _ in range(3):
-                run()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 50
-            e0.record()
-            for _ in range(reps):
-                run()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
-            kv_bytes = b * hkv * L * hd * 2 * 2
-            io_bytes = 2 * b * nb * hq * hd * 2
-            gbs = (kv_bytes + io_bytes) / (us * 1e-6) / 1e9
-            print(json.dumps({"metric": "block-causal attention alone", "prefix": P, "batch": b, "rows": b * nb,
-                              "heads": f"{hq}q/{hkv}kv x {hd}", "us": round(us, 2),
-                              "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                           "algorithmic_bytes": kv_bytes + io_bytes}}), flush=True)
-            del kc, vc, q, out, ws
+            for variant, hi, vsrc in (("block rows", block_hi, vcs), ("causal rows", causal_hi, vcs),
+                                      ("block rows, fp16 V cache", block_hi, vcs16)):
+                def run(i):
+                    tm.block_causal_attn(q, kcs[i], vsrc[i], ss, hi, out, 1.0 / math.sqrt(hd), max_rows_per_seq=nb,
+                                         max_hi=L, ws=ws)
+                for i in range(min(nsets, 4)):
+                    run(i)
+                torch.cuda.synchronize()
+                per = []
+                for _ in range(20):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for i in range(nsets):
+                        run(i)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    per.append(e0.elapsed_time(e1) * 1e3 / nsets)
+                us = float(np.median(per))
+                kv_bytes = b * hkv * L * hd * 2 * 2 if variant != "causal rows" else \
+                    b * hkv * (P + nb) * hd * 2 * 2
+                io_bytes = 2 * b * nb * hq * hd * 2
+                gbs = (kv_bytes + io_bytes) / (us * 1e-6) / 1e9
+                print(json.dumps({"metric": "block-causal attention alone", "variant": variant, "prefix": P, "batch": b,
+                                  "rows": b * nb, "heads": f"{hq}q/{hkv}kv x {hd}", "us": round(us, 2),
+                                  "us_p10": round(float(np.percentile(per, 10)), 2),
+                                  "us_p90": round(float(np.percentile(per, 90)), 2),
+                                  "buffer_sets": nsets, "timed_launches": 20 * nsets,
+                                  "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                               "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                               "algorithmic_bytes": kv_bytes + io_bytes}}), flush=True)
+            del kcs, vcs, vcs16, q, out, ws
             torch.cuda.empty_cache()
+    print(json.dumps({"metric": "clocks", "before": clocks0, "after": gpu_clocks()}), flush=True)
 
 
 def attention_split_sweep(args):
@@ -245,6 +281,69 @@ def step_flops(shape, rows):
     p_layer = ((qd + 2 * shape.n_kv_heads * shape.head_dim) * shape.d_model + qd * shape.d_model
                + 3 * shape.d_ffn * shape.d_model)
     return 2.0 * rows * (shape.n_layers * p_layer + shape.vocab * shape.d_model)
+
+
+def quadratic_sweep(args):
+    """Quadratic self-speculation (TRI_QUADSPEC) on the 8B-class decoder at
+    batch 1 after a 512-token prompt, k in {4, 8, 16, 32}: one forward per
+    round over 1 + k + (k+1)^2 rows (the drafts verified, plus a block of k+1
+    [MASK] rows for every accept length).  Per k: the forward's time, the
+    natural tokens/s (random-init drafts are never accepted), and a
+    controlled replay (carried drafts replaced by the GPU's own greedy
+    continuation up to a* = min(6, k), mismatch forced there) next to linear
+    self-speculation under the same a*: the pages report a higher TPF for the
+    quadratic mode and say the kernel and mask limit its device efficiency
+    ([Notes §8.1]; [Blog], performance highlights)."""
+    import torch
+    import seeded
+    import self_speculative_lm_amd as tm
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    shape = seeded.MODEL_8B
+    model = build_model(shape, dev)
+    prompt = seeded.prompt(args.prompt, shape.vocab)
+    for k in (4, 8, 16, 32):
+        rows = 1 + k + (k + 1) ** 2
+        rounds = 12
+        n_ref = (rounds + 4) * (k + 1) + k + 2
+        max_ctx = args.prompt + n_ref + 2 * k + 64
+        sess = tm.Session(model, max_batch=1, max_ctx=max_ctx, max_rows=max(args.max_rows, rows), device=dev)
+        sess.prefill(0, prompt)
+        for _ in range(n_ref):
+            sess.decode_step(tm.TRI_AR, 1)
+        ref = sess.state(0)[0]
+        line = {"metric": "quadratic self-speculation, 8B-class, batch 1", "k": k, "rows_per_forward": rows}
+        for label, a_star in (("natural", -1), ("controlled", min(6, k))):
+            res = {}
+            for mode, fwd_per_round in ((tm.TRI_QUADSPEC, 1), (tm.TRI_SELFSPEC, 2)):
+                sess.prefill(0, prompt)
+                if a_star >= 0:
+                    sess.set_draft_override(0, ref, a_star)
+                for _ in range(2):
+                    sess.decode_step(mode, k)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                c = 0
+                accepts = []
+                for _ in range(rounds):
+                    _, st = sess.decode_step(mode, k)
+                    c += st[0][0]
+                    accepts.append(st[0][2])
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
+                got = sess.state(0)[0]
+                sess.set_draft_override(0, None, -1)
+                res["quadratic" if mode == tm.TRI_QUADSPEC else "linear"] = {
+                    "tok_s": round(c / dt, 1), "tokens_per_round": round(c / rounds, 3),
+                    "tpf": round(c / (rounds * fwd_per_round), 3), "ms_per_round": round(dt * 1e3 / rounds, 3),
+                    "matches_ar": got == ref[: len(got)], "accepts": sorted(set(accepts))}
+            line[label] = res
+            if label == "controlled":
+                line["controlled"]["a_star"] = a_star
+        log(f"k={k}: {line}")
+        print(json.dumps(line), flush=True)
+        del sess
+        torch.cuda.empty_cache()
 
 
 def concurrency_sweep(args):
@@ -547,6 +646,8 @@ def main():
                     help="speed-of-light analysis (serial denoising + parallel pass) at 1 and 8 sequences")
     ap.add_argument("--diffusion", action="store_true",
                     help="8B-class diffusion mode at 1/4/16 sequences and thresholds 0.5/0.7/0.9, plus AR at 16")
+    ap.add_argument("--quad", action="store_true",
+                    help="quadratic self-speculation on the 8B-class model at k = 4..32, next to linear")
     ap.add_argument("--long14b", action="store_true",
                     help="14B-class self-speculation with the draft LoRA behind a 16384-token prefix")
     ap.add_argument("--calib-copy", action="store_true",
@@ -573,6 +674,9 @@ def main():
         return
     if args.long14b:
         long_prefix_14b(args)
+        return
+    if args.quad:
+        quadratic_sweep(args)
         return
 
     import numpy as np

@@ -46,7 +46,7 @@ enum {
 
 /* Decoding modes: one checkpoint, three modes chosen by one setting
  * [Blog, deployment section; Notes §5]. */
-enum { TRI_AR = 0, TRI_DIFFUSION = 1, TRI_SELFSPEC = 2 };
+enum { TRI_AR = 0, TRI_DIFFUSION = 1, TRI_SELFSPEC = 2, TRI_QUADSPEC = 3 };
 
 /* Storage types: weights, activations fed to GEMMs, queries and the KV cache.
  * Accumulation, softmax, the residual stream and logits are always float32. */
@@ -140,6 +140,18 @@ int tri_prefill(tri_session* session, int seq, const int32_t* tokens, int n);
  *                  forward over the k = block drafts; commits the longest
  *                  matching prefix plus the AR token after it, 1..k+1 tokens,
  *                  lossless against greedy AR [Notes §5.3; Digest, Method].
+ *   TRI_QUADSPEC:  one round of quadratic self-speculation [Notes §8.1; Blog,
+ *                  performance highlights], one forward: the pending tokens
+ *                  and the n drafts carried from the previous round as causal
+ *                  rows (they verify the drafts: accept length a), plus for
+ *                  every b = 0..n a block of k+1 = block+1 [MASK] rows at
+ *                  L+b..L+b+k that sees the clean prefix [0, L+b) and itself
+ *                  (LoRA rows); commits the a+1 verified tokens (lossless
+ *                  against greedy AR) and carries block a's next k drafts.
+ *                  n = 0 on the first round and after any other step,
+ *                  prefill, kv_append or kv_rollback of the sequence.  Needs
+ *                  block <= 63 and pending + n + (n+1)(block+1) rows per
+ *                  sequence within max_rows; out_stats counts one forward.
  * block in [1, 64].  out_tokens: host [batch][block+1], the committed tokens
  * of each sequence, -1 padded.  out_stats: host [batch] (may be NULL).
  * Synchronous (returns after the step's results are on the host). */

@@ -12,11 +12,11 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from ._lib import (TRI_AR, TRI_BF16, TRI_BF16_V16, TRI_DIFFUSION, TRI_F32, TRI_SELFSPEC, ModelDesc, SeqStats, TriError,  # noqa: F401
+from ._lib import (TRI_AR, TRI_BF16, TRI_BF16_V16, TRI_DIFFUSION, TRI_F32, TRI_QUADSPEC, TRI_SELFSPEC, ModelDesc, SeqStats, TriError,  # noqa: F401
                    check, lib)
 
 __all__ = ["Model", "Session", "block_causal_attn", "sample_commit", "verify_accept", "weight_names", "choose_modes",
-           "TriError", "TRI_AR", "TRI_DIFFUSION", "TRI_SELFSPEC", "TRI_F32", "TRI_BF16", "TRI_BF16_V16"]
+           "TriError", "TRI_AR", "TRI_DIFFUSION", "TRI_SELFSPEC", "TRI_QUADSPEC", "TRI_F32", "TRI_BF16", "TRI_BF16_V16"]
 
 
 def _torch():

@@ -6,7 +6,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtrimode.so")
 
 TRI_OK, TRI_EINVAL, TRI_ECAPACITY, TRI_ESTATE, TRI_EHIP, TRI_ENUMERIC = 0, -1, -2, -3, -4, -5
-TRI_AR, TRI_DIFFUSION, TRI_SELFSPEC = 0, 1, 2
+TRI_AR, TRI_DIFFUSION, TRI_SELFSPEC, TRI_QUADSPEC = 0, 1, 2, 3
 TRI_F32, TRI_BF16, TRI_BF16_V16 = 0, 1, 2
 
 _ERR_NAMES = {TRI_EINVAL: "TRI_EINVAL", TRI_ECAPACITY: "TRI_ECAPACITY", TRI_ESTATE: "TRI_ESTATE",

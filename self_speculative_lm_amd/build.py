@@ -40,37 +40,62 @@ def compile_flags(src: str) -> list:
             "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc")]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source to an object (in parallel), then link the library."""
-    objdir = os.path.join(HERE, "_build")
+# Host-code sanitizers (AddressSanitizer + UndefinedBehaviorSanitizer) for a
+# checking build of the runtime: each -fsanitize applies to the host pass only
+# (device code is built as usual).  The library then needs the sanitizer
+# runtime preloaded (sanitizer_runtime()).
+SANITIZE_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the HIP toolchain."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = out.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        rt = subprocess.run(["/opt/rocm/llvm/bin/clang", "-print-resource-dir"], capture_output=True, text=True)
+        path = os.path.join(rt.stdout.strip(), "lib", "linux", "libclang_rt.asan-x86_64.so")
+    return path
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str = OUT) -> str:
+    """Compile every source to an object (in parallel), then link the library.
+    sanitize: the host-sanitizer checking build (objects and library at `out`'s
+    directory, never the in-tree library)."""
+    objdir = os.path.join(os.path.dirname(out) if sanitize else HERE, "_build_san" if sanitize else "_build")
     os.makedirs(objdir, exist_ok=True)
     procs = []
     for s in SOURCES:
         src = os.path.join(HERE, "csrc", s)
         obj = os.path.join(objdir, s + ".o")
-        cmd = [hipcc(), *compile_flags(src), "-c", src, "-o", obj]
+        flags = compile_flags(src)
+        if sanitize:
+            flags = [f for f in flags if f != "-O3"] + SANITIZE_FLAGS
+        cmd = [hipcc(), *flags, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((obj, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
     failed = []
     for obj, cmd, p in procs:
-        out, _ = p.communicate()
+        log, _ = p.communicate()
         if p.returncode != 0:
-            failed.append((cmd, out))
+            failed.append((cmd, log))
     if failed:
-        for cmd, out in failed:
-            sys.stderr.write(" ".join(cmd) + "\n" + out)
+        for cmd, log in failed:
+            sys.stderr.write(" ".join(cmd) + "\n" + log)
         raise RuntimeError(f"hipcc failed for {len(failed)} source(s)")
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *[o for o, _, _ in procs], "-o", tmp]
+    if sanitize:
+        cmd += ["-fsanitize=address,undefined", "-shared-libsan"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"link failed with exit code {r.returncode}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

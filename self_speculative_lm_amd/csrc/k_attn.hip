@@ -62,6 +62,7 @@ struct AttnArgs {
   float* part_o;   // [nsplit][rows][hq][HD]
   float* part_ml;  // [nsplit][rows][hq][2]
   int qgroups, nz;  // query groups per (split, sequence x kv head); n_seq * hkv
+  int force_part;   // write partials even with one split (a combine follows)
 };
 
 __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
     l = sum_xor32(sum_xor16(l));
     if (!valid[q]) continue;
     // lane (j, g) holds O^T[16dt + 4g + r][query j]
-    if (a.nsplit == 1) {
+    if (a.nsplit == 1 && !a.force_part) {
       bf16_t* op = a.out + ((size_t)qrow(q) * a.hq + qhead(q)) * HD + 4 * g;
       const float inv = 1.f / l;
 #pragma unroll
@@ -472,11 +473,89 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(const float* part_o, 
   if (d < hd) Elem<T>::store(out, ((size_t)row * hq + head) * hd + d, O * inv);
 }
 
+// The split merge of attn_combine_kernel followed, for a row of a
+// quadratic-speculation block (row_blk[row] >= 0), by its block's keys: the
+// blk_len keys of the forward's row scratch starting at row row_blk[row]
+// (scores q.k scaled into the log2 domain, one thread per key, then one
+// online step over the block); then O * (1 / L).  A row without a block
+// gets attn_combine_kernel's bits (the AR pathway's rows of the same
+// forward are the AR rows).
+template <typename T>
+__global__ __launch_bounds__(512) void attn_qcombine_kernel(const float* part_o, const float* part_ml,
+                                                            const int32_t* row_hi, const int32_t* row_blk,
+                                                            const T* q, const T* ks, const T* vs, int blk_len,
+                                                            int rows, int hq, int hkv, int kv_split, int nsplit,
+                                                            float scale_log2, T* out) {
+  constexpr int B = 16;
+  __shared__ float sc[4][64];
+  const int row = blockIdx.x, hl = (int)threadIdx.x / HD, head = blockIdx.y * 4 + hl, d = threadIdx.x % HD;
+  const bool hv = head < hq;
+  const int hh = hv ? head : hq - 1;
+  const int hi = row_hi[row];
+  float M = -1e30f, L = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < nsplit; c0 += B) {
+    float m[B], l[B], o[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const size_t base = ((size_t)min(c0 + i, nsplit - 1) * rows + row) * hq + hh;
+      m[i] = part_ml[base * 2];
+      l[i] = part_ml[base * 2 + 1];
+      o[i] = part_o[base * HD + d];
+    }
+    const int ns = (hi + kv_split - 1) / kv_split;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if (c0 + i == 0) {
+        M = m[0];
+        L = l[0];
+        O = o[0];
+      } else if (c0 + i < ns) {
+        const float Mn = fmaxf(M, m[i]);
+        const float wa = exp2f(M - Mn), wb = exp2f(m[i] - Mn);
+        L = fmaf(l[i], wb, L * wa);
+        O = fmaf(o[i], wb, O * wa);
+        M = Mn;
+      }
+    }
+    if (c0 + B >= ns) break;
+  }
+  const int blk = row_blk[row];
+  if (blk >= 0) {  // the same for every thread of the workgroup
+    const int kvh = hh / (hq / hkv);
+    if (d < blk_len) {
+      const T* qp = q + ((size_t)row * hq + hh) * HD;
+      const T* kp = ks + ((size_t)(blk + d) * hkv + kvh) * HD;
+      float acc = 0.f;
+      for (int e = 0; e < HD; ++e) acc = fmaf(Elem<T>::load(qp, e), Elem<T>::load(kp, e), acc);
+      sc[hl][d] = acc * scale_log2;
+    }
+    __syncthreads();
+    float m2 = -1e30f;
+    for (int j = 0; j < blk_len; ++j) m2 = fmaxf(m2, sc[hl][j]);
+    float l2 = 0.f, o2 = 0.f;
+    for (int j = 0; j < blk_len; ++j) {
+      const float p = exp2f(sc[hl][j] - m2);
+      l2 += p;
+      o2 = fmaf(p, Elem<T>::load(vs, ((size_t)(blk + j) * hkv + kvh) * HD + d), o2);
+    }
+    const float Mn = fmaxf(M, m2);
+    const float wa = exp2f(M - Mn), wb = exp2f(m2 - Mn);
+    L = fmaf(l2, wb, L * wa);
+    O = fmaf(o2, wb, O * wa);
+  }
+  const float inv = 1.f / L;
+  if (hv) Elem<T>::store(out, ((size_t)row * hq + head) * HD + d, O * inv);
+}
+
 // float32 path: one wave per (row, head), keys 64 at a time, one pass.
+// A row of a quadratic-speculation block (row_blk[row] >= 0) continues the
+// same online pass over its block's blk_len keys from the row scratch
+// ks / vs [rows][hkv][hd].
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, const float* kc, const float* vc,
                                                        const int32_t* seq_start, const int32_t* slot_seq,
                                                        int n_seq, const int32_t* row_hi, int hq, int hkv, int hd,
-                                                       int ctx, float scale, float* out) {
+                                                       int ctx, float scale, float* out, const int32_t* row_blk,
+                                                       const float* ks, const float* vs, int blk_len) {
   __shared__ float qs[HD];
   const int row = blockIdx.x, head = blockIdx.y, lane = threadIdx.x;
   int seq = 0;
@@ -514,6 +593,33 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, const floa
       if (lane + 64 < hd) o1 = fmaf(pj, vb[(size_t)(lane + 64) * ctx + j0 + jj], o1);
     }
     m = m_new;
+  }
+  const int blk = row_blk ? row_blk[row] : -1;
+  if (blk >= 0) {
+    const int key = lane;
+    float s = -INFINITY;
+    if (key < blk_len) {
+      float acc = 0.f;
+      const float* kp = ks + ((size_t)(blk + key) * hkv + kvh) * hd;
+      for (int d = 0; d < hd; ++d) acc = fmaf(qs[d], kp[d], acc);
+      s = acc * scale;
+    }
+    float cmax = s;
+    for (int off = 32; off > 0; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
+    const float m_new = fmaxf(m, cmax);
+    const float alpha = expf(m - m_new);
+    const float p = (key < blk_len) ? expf(s - m_new) : 0.f;
+    float ps = p;
+    for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+    l = fmaf(l, alpha, ps);
+    o0 *= alpha;
+    o1 *= alpha;
+    for (int jj = 0; jj < blk_len; ++jj) {
+      const float pj = __shfl(p, jj);
+      const float* vp = vs + ((size_t)(blk + jj) * hkv + kvh) * hd;
+      if (lane < hd) o0 = fmaf(pj, vp[lane], o0);
+      if (lane + 64 < hd) o1 = fmaf(pj, vp[lane + 64], o1);
+    }
   }
   float* op = out + ((size_t)row * hq + head) * hd;
   if (lane < hd) op[lane] = o0 / l;
@@ -596,10 +702,12 @@ size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split) {
 
 hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   if (L.rows <= 0) return hipSuccess;
+  if (L.row_blk && (L.blk_len < 1 || L.blk_len > 64 || !L.k_scr || !L.v_scr)) return hipErrorInvalidValue;
   if (dtype == TRI_F32) {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(L.rows, L.hq), dim3(64), 0, st, static_cast<const float*>(L.q),
                        static_cast<const float*>(L.kc), static_cast<const float*>(L.vc), L.seq_start, L.slot_seq,
-                       L.n_seq, L.row_hi, L.hq, L.hkv, L.hd, L.ctx, L.scale, static_cast<float*>(L.out));
+                       L.n_seq, L.row_hi, L.hq, L.hkv, L.hd, L.ctx, L.scale, static_cast<float*>(L.out), L.row_blk,
+                       static_cast<const float*>(L.k_scr), static_cast<const float*>(L.v_scr), L.blk_len);
     return hipGetLastError();
   }
   AttnArgs a;
@@ -617,6 +725,7 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   a.nsplit = (L.max_hi + L.kv_split - 1) / L.kv_split;
   a.scale_log2 = L.scale * 1.4426950408889634f;
   a.out = static_cast<bf16_t*>(L.out);
+  a.force_part = L.row_blk != nullptr;
   const size_t np = (size_t)a.nsplit * L.rows * L.hq;
   a.part_o = L.part;
   a.part_ml = L.part + np * HD;
@@ -647,7 +756,15 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
     hipLaunchKernelGGL((attn_bf16_kernel<4, 2, 2>), grid, dim3(512), 0, st, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
+  if (e != hipSuccess) return e;
+  if (L.row_blk) {
+    hipLaunchKernelGGL(attn_qcombine_kernel<bf16_t>, dim3(L.rows, (L.hq + 3) / 4), dim3(4 * HD), 0, st, a.part_o,
+                       a.part_ml, L.row_hi, L.row_blk, a.q, static_cast<const bf16_t*>(L.k_scr),
+                       static_cast<const bf16_t*>(L.v_scr), L.blk_len, L.rows, L.hq, L.hkv, L.kv_split, a.nsplit,
+                       a.scale_log2, a.out);
+    return hipGetLastError();
+  }
+  if (a.nsplit == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(L.rows, (L.hq + 3) / 4), dim3(4 * HD), 0, st, a.part_o, a.part_ml,
                      L.row_hi, L.rows, L.hq, HD, L.kv_split, a.nsplit, a.out);
   return hipGetLastError();

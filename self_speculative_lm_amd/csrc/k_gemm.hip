@@ -573,6 +573,16 @@ void launch_wide(const GemmArgs& a, const BigGrid& g, bool chain, bool swiglu, b
     launch_wide_form<BIGM_MT, NCH, BIGM_FPW>(a, g, chain, swiglu, st);
 }
 
+// Passes of the large-M kernel as long as possible: the largest NCH <= 8
+// dividing the stages per split (one pass per split for every 8B/14B
+// projection plan).
+static int wide_nch(const GemmPlan& plan) {
+  const int ps = plan.Ks / KC;
+  for (int c : {8, 6, 5, 4, 3, 2})
+    if (ps % c == 0) return c;
+  return 1;
+}
+
 int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant) {
   if (dtype != TRI_BF16) return p.S;
   return gemm_use_big(M, N, K) ? big_grid(p, M, N, invariant).nyg : p.S;
@@ -604,15 +614,7 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
       const bool tall = big_tall(M);
       const int bpw = tall ? TALL_BPW : BIGM_BPW;
       a.ntiles = ((a.nfb + bpw - 1) / bpw + 7) / 8 * 8 * g.ntm * g.nyg;
-      // passes as long as possible: the largest NCH <= 8 dividing the stages
-      // per split (one pass per split for every 8B/14B projection plan)
-      const int ps = plan.Ks / KC;
-      int nch = 1;
-      for (int c : {8, 6, 5, 4, 3, 2})
-        if (ps % c == 0) {
-          nch = c;
-          break;
-        }
+      const int nch = wide_nch(plan);
       const bool chain = invariant && g.cs > 1, sw = swiglu_out != nullptr;
       switch (nch) {
         case 1: launch_wide<1>(a, g, chain, sw, tall, st); break;
@@ -641,6 +643,55 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
                        static_cast<const float*>(W), N, P);
   }
   return hipGetLastError();
+}
+
+// One past the highest packed W element that launch_gemm's kernel reads for
+// these arguments: both kernels' address arithmetic (block j*G + g of the
+// step-major layout, the wave's fragment, lane 63's 8 elements, the last
+// ring refill of the last pass) evaluated on the host over every workgroup
+// and wave of the launch grid.  The packed matrix holds
+// gemm_packed_bytes / 2 elements; 0 for float32 models.
+size_t gemm_w_reach(int dtype, const GemmPlan& plan, int M, int N, int K, bool invariant) {
+  if (dtype != TRI_BF16 || M <= 0) return 0;
+  const int nfb = (N + GROUP - 1) / GROUP, G = nfb * plan.S;
+  const size_t wstep = (size_t)G * (WAVES_PER_WG * 512);
+  size_t reach = 0;
+  if (gemm_use_big(M, N, K)) {
+    const BigGrid bg = big_grid(plan, M, N, invariant);
+    const bool tall = big_tall(M);
+    const int FPW = tall ? TALL_FPW : BIGM_FPW, BPW = tall ? TALL_BPW : BIGM_BPW;
+    const int nch = wide_nch(plan), NS = nch * KSTEPS, npass_split = plan.Ks / (nch * KC);
+    const long ntiles = (long)((nfb + BPW - 1) / BPW + 7) / 8 * 8 * bg.ntm * bg.nyg;
+    for (long id = 0; id < ntiles; ++id) {
+      const long q = id >> 3, per = (long)bg.ntm * bg.nyg;
+      const long fgx = (q / per) * 8 + (id & 7), rem = q - (q / per) * per;
+      if (fgx * BPW >= nfb) continue;
+      const int yg = (int)(rem / bg.ntm);
+      for (int wave = 0; wave < BIGM_WAVES; ++wave) {
+        const long blkx = fgx * BPW + (wave * FPW) / 8;
+        const long bx = blkx < nfb ? blkx : nfb - 1;
+        const int fg0 = (wave * FPW) % 8;
+        for (int pp = 0; pp < bg.cs * npass_split; ++pp) {
+          const int y = yg * bg.cs + pp / npass_split, p = pp % npass_split;
+          const size_t base = ((size_t)(p * NS) * G + (size_t)y * nfb + bx) * 4096 + fg0 * 512 + 63 * 8;
+          reach = std::max(reach, base + (size_t)(NS - 1) * wstep + (FPW - 1) * 512 + 8);
+        }
+      }
+    }
+  } else {
+    const int mt = M >= 64 ? 4 : (M + 15) / 16;
+    const int NS = plan.nch * KSTEPS, npass = plan.Ks / (plan.nch * KC);
+    const long ntiles = (long)G * ((M + 16 * mt - 1) / (16 * mt));
+    for (long b = 0; b < ntiles; ++b) {
+      const int g = (int)(b % G);
+      for (int wave = 0; wave < WAVES_PER_WG; ++wave)
+        for (int p = 0; p < npass; ++p) {
+          const size_t base = (size_t)g * (WAVES_PER_WG * 512) + wave * 512 + 63 * 8 + (size_t)p * NS * wstep;
+          reach = std::max(reach, base + (size_t)(NS - 1) * wstep + 8);
+        }
+    }
+  }
+  return reach;
 }
 
 }  // namespace tri

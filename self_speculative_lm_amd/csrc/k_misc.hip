@@ -106,7 +106,14 @@ __global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* __restr
 // into the cache slot of the row's position (V transposed).
 // Grid (rows, heads / 4), one wave per (row, head) of the hq + 2*hkv heads:
 // q and k heads rotate pairs (c, c + hd/2), v heads are copied to the
-// transposed V cache.
+// transposed V cache.  A row of a quadratic-speculation block (blk[r] >= 0)
+// writes its k and v to the forward's row scratch instead, [r][hkv][hd]
+// each (its keys are seen by its own block only, never through the cache).
+struct BlockScratch {
+  const int32_t* blk;  // per row: first row of its block, or -1 (NULL: no block rows)
+  void* k;             // [rows][hkv][hd], the model's storage type
+  void* v;             // [rows][hkv][hd]
+};
 constexpr int ROPE_HEADS = 4;  // waves (heads) per workgroup
 template <typename T>
 __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* __restrict__ P, int nslots,
@@ -115,10 +122,12 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
                                                                   const int32_t* row_pos,
                                                                   const float* __restrict__ rope,
                                                                   T* __restrict__ qout, T* __restrict__ kc,
-                                                                  T* __restrict__ vc, int ctx, size_t css) {
+                                                                  T* __restrict__ vc, int ctx, size_t css,
+                                                                  BlockScratch bs) {
   const int r = blockIdx.x, h = blockIdx.y * ROPE_HEADS + (int)(threadIdx.x >> 6);
   if (h >= hq + 2 * hkv) return;
   const int pos = row_pos[r], seq = row_seq[r];
+  const bool scr = bs.blk && bs.blk[r] >= 0;
   const int half = hd / 2;
   const size_t rb = (size_t)r * (hq + 2 * hkv) * hd + (size_t)h * hd;
   if (h < hq + hkv) {
@@ -134,16 +143,21 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
         Elem<T>::store(qout, o, ra);
         Elem<T>::store(qout, o + half, rbv);
       } else {
-        const size_t o = (size_t)seq * css + ((size_t)(h - hq) * ctx + pos) * hd + c;
-        Elem<T>::store(kc, o, ra);
-        Elem<T>::store(kc, o + half, rbv);
+        T* kd = scr ? static_cast<T*>(bs.k) : kc;
+        const size_t o = scr ? ((size_t)r * hkv + (h - hq)) * hd + c
+                             : (size_t)seq * css + ((size_t)(h - hq) * ctx + pos) * hd + c;
+        Elem<T>::store(kd, o, ra);
+        Elem<T>::store(kd, o + half, rbv);
       }
     }
   } else {
     const int kh = h - hq - hkv;
     for (int dd = threadIdx.x & 63; dd < hd; dd += 64) {
       const float val = slot_sum(P, nslots, stride, rb + dd);
-      Elem<T>::store(vc, (size_t)seq * css + ((size_t)kh * hd + dd) * ctx + pos, val);
+      if (scr)
+        Elem<T>::store(static_cast<T*>(bs.v), ((size_t)r * hkv + kh) * hd + dd, val);
+      else
+        Elem<T>::store(vc, (size_t)seq * css + ((size_t)kh * hd + dd) * ctx + pos, val);
     }
   }
 }
@@ -152,7 +166,8 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
 // lane four consecutive columns of both halves (float4 slot and table loads),
 // four heads per wave.  Same arithmetic per element as rope_kv_kernel.  VF16
 // (bf16 models): V is written in the attention's fp16 form, and *vsat is set
-// when a value saturates it.
+// when a value saturates it.  Block rows write k and v (bf16, not the fp16
+// form) to the row scratch as rope_kv_kernel does.
 constexpr int ROPE128_HPW = 4;                    // heads per wave
 constexpr int ROPE128_HEADS = 4 * ROPE128_HPW;    // heads per 256-thread workgroup
 template <typename T, bool VF16 = false>
@@ -160,13 +175,15 @@ __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict
                                                          int hq, int hkv, const int32_t* row_seq,
                                                          const int32_t* row_pos, const float* __restrict__ rope,
                                                          T* __restrict__ qout, T* __restrict__ kc,
-                                                         T* __restrict__ vc, int ctx, size_t css, int32_t* vsat) {
+                                                         T* __restrict__ vc, int ctx, size_t css, int32_t* vsat,
+                                                         BlockScratch bs) {
   constexpr int hd = 128, half = 64;
   const int r = blockIdx.x;
   const int h = blockIdx.y * ROPE128_HEADS + (int)(threadIdx.x >> 4);
   if (h >= hq + 2 * hkv) return;
   const int c = 4 * (threadIdx.x & 15);
   const int pos = row_pos[r], seq = row_seq[r];
+  const bool scr = bs.blk && bs.blk[r] >= 0;
   const size_t rb = (size_t)r * (hq + 2 * hkv) * hd + (size_t)h * hd;
   const f32x4 xa = slot_sum4(P, nslots, stride, rb + c);
   const f32x4 xb = slot_sum4(P, nslots, stride, rb + c + half);
@@ -184,11 +201,20 @@ __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict
       const size_t o = ((size_t)r * hq + h) * hd + c;
       Elem<T>::store4(qout, o, ra);
       Elem<T>::store4(qout, o + half, rbv);
+    } else if (scr) {
+      const size_t o = ((size_t)r * hkv + (h - hq)) * hd + c;
+      Elem<T>::store4(static_cast<T*>(bs.k), o, ra);
+      Elem<T>::store4(static_cast<T*>(bs.k), o + half, rbv);
     } else {
       const size_t o = (size_t)seq * css + ((size_t)(h - hq) * ctx + pos) * hd + c;
       Elem<T>::store4(kc, o, ra);
       Elem<T>::store4(kc, o + half, rbv);
     }
+  } else if (scr) {
+    const int kh = h - hq - hkv;
+    const size_t o = ((size_t)r * hkv + kh) * hd + c;
+    Elem<T>::store4(static_cast<T*>(bs.v), o, xa);
+    Elem<T>::store4(static_cast<T*>(bs.v), o + half, xb);
   } else {
     const int kh = h - hq - hkv;
     const size_t o = (size_t)seq * css + (size_t)kh * hd * ctx + pos;
@@ -465,36 +491,37 @@ hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, si
 hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, int rows, int hq, int hkv,
                           int hd, const int32_t* row_seq, const int32_t* row_pos, const float* rope,
                           void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st, bool v_f16,
-                          int32_t* vsat) {
+                          int32_t* vsat, const int32_t* row_blk, void* kscr, void* vscr) {
   if (rows <= 0) return hipSuccess;
   if (nslots > MAX_SLOTS || (v_f16 && (dtype != TRI_BF16 || hd != 128))) return hipErrorInvalidValue;
-  if (v_f16) {
-    const dim3 grid128(rows, (hq + 2 * hkv + ROPE128_HEADS - 1) / ROPE128_HEADS);
-    hipLaunchKernelGGL((rope_kv128_kernel<bf16_t, true>), grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
-                       row_seq, row_pos, rope, static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
-                       static_cast<bf16_t*>(vc), ctx, css, vsat);
-    return hipGetLastError();
-  }
+  if (row_blk && (!kscr || !vscr)) return hipErrorInvalidValue;
+  const BlockScratch bs{row_blk, kscr, vscr};
   if (hd == 128) {
     const dim3 grid128(rows, (hq + 2 * hkv + ROPE128_HEADS - 1) / ROPE128_HEADS);
+    if (v_f16) {
+      hipLaunchKernelGGL((rope_kv128_kernel<bf16_t, true>), grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
+                         row_seq, row_pos, rope, static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
+                         static_cast<bf16_t*>(vc), ctx, css, vsat, bs);
+      return hipGetLastError();
+    }
     TRI_DISPATCH(dtype,
                  hipLaunchKernelGGL(rope_kv128_kernel<float>, grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
                                     row_seq, row_pos, rope, static_cast<float*>(qout), static_cast<float*>(kc),
-                                    static_cast<float*>(vc), ctx, css, vsat),
+                                    static_cast<float*>(vc), ctx, css, vsat, bs),
                  hipLaunchKernelGGL(rope_kv128_kernel<bf16_t>, grid128, dim3(256), 0, st, P, nslots, stride, hq,
                                     hkv, row_seq, row_pos, rope, static_cast<bf16_t*>(qout),
-                                    static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, css, vsat));
+                                    static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, css, vsat, bs));
     return hipGetLastError();
   }
   const dim3 grid(rows, (hq + 2 * hkv + ROPE_HEADS - 1) / ROPE_HEADS);
   TRI_DISPATCH(dtype,
                hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(64 * ROPE_HEADS), 0, st, P, nslots, stride,
                                   hq, hkv, hd, row_seq, row_pos, rope, static_cast<float*>(qout),
-                                  static_cast<float*>(kc), static_cast<float*>(vc), ctx, css),
+                                  static_cast<float*>(kc), static_cast<float*>(vc), ctx, css, bs),
                hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(64 * ROPE_HEADS), 0, st, P, nslots,
                                   stride, hq, hkv, hd, row_seq, row_pos, rope,
                                   static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
-                                  static_cast<bf16_t*>(vc), ctx, css));
+                                  static_cast<bf16_t*>(vc), ctx, css, bs));
   return hipGetLastError();
 }
 

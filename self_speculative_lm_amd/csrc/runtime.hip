@@ -75,11 +75,14 @@ struct Seq {
   int a_star = -1;
   // controlled commit rate (benchmark hook): per-forward commit counts of a diffusion block
   std::vector<int32_t> sched;
+  // quadratic self-speculation: drafts for positions L .. L+k-1 carried from
+  // the previous round (empty: the next round starts without drafts)
+  std::vector<int32_t> qdrafts;
 };
 
 // Row metadata of one forward: a host (pinned) mirror and a device copy.
 struct MetaLayout {
-  size_t tok, pos, hi, seq, lora, kind, seq_start, slot_seq, block_start, sidx, didx, size;
+  size_t tok, pos, hi, seq, lora, kind, blk, seq_start, slot_seq, block_start, sidx, didx, size;
 };
 MetaLayout meta_layout(int max_rows, int max_batch) {
   MetaLayout L;
@@ -95,6 +98,7 @@ MetaLayout meta_layout(int max_rows, int max_batch) {
   L.seq = take(max_rows);
   L.lora = take(max_rows);
   L.kind = take(max_rows);
+  L.blk = take(max_rows);
   L.seq_start = take(max_batch + 1);
   L.slot_seq = take(max_batch);
   L.block_start = take(max_batch + 1);
@@ -105,11 +109,11 @@ MetaLayout meta_layout(int max_rows, int max_batch) {
 }
 
 struct Meta {
-  int32_t *tok, *pos, *hi, *seq, *lora, *kind, *seq_start, *slot_seq, *block_start, *sidx, *didx;
+  int32_t *tok, *pos, *hi, *seq, *lora, *kind, *blk, *seq_start, *slot_seq, *block_start, *sidx, *didx;
 };
 Meta meta_ptrs(int32_t* base, size_t off, const MetaLayout& L) {
   int32_t* b = base + off;
-  return Meta{b + L.tok,  b + L.pos,       b + L.hi,          b + L.seq,         b + L.lora, b + L.kind,
+  return Meta{b + L.tok,  b + L.pos,       b + L.hi,          b + L.seq,         b + L.lora, b + L.kind, b + L.blk,
               b + L.seq_start, b + L.slot_seq, b + L.block_start, b + L.sidx, b + L.didx};
 }
 
@@ -121,20 +125,25 @@ MetaLayout forward_layout(int n, int max_rows, int max_batch) {
   return meta_layout(std::min((n + 63) & ~63, max_rows), max_batch);
 }
 
-// Host-side rows of one forward.
+// Host-side rows of one forward.  blk: per row the first row of its
+// quadratic-speculation block or -1 (only filled when blk_len > 0: the rows
+// of a block attend to the cache keys [0, hi) and to the blk_len rows of
+// their block).
 struct HostRows {
-  std::vector<int32_t> tok, pos, hi, seq, lora, kind;
+  std::vector<int32_t> tok, pos, hi, seq, lora, kind, blk;
+  int blk_len = 0;
   std::vector<int32_t> seq_start{0};  // per slot (one slot per participating sequence)
   std::vector<int32_t> slot_seq;
   std::vector<int32_t> block_start;   // per block (empty: no blocks)
   int n() const { return (int)tok.size(); }
-  void add(int t, int p, int h, int s, int l, int k) {
+  void add(int t, int p, int h, int s, int l, int k, int b = -1) {
     tok.push_back(t);
     pos.push_back(p);
     hi.push_back(h);
     seq.push_back(s);
     lora.push_back(l);
     kind.push_back(k);
+    blk.push_back(b);
   }
   void close_slot(int s) {
     seq_start.push_back(n());
@@ -168,6 +177,8 @@ struct tri_session {
   float* part;
   float* part2;
   void* attn_ws;
+  void* kscr;  // quadratic-speculation block rows' K and V [max_rows][hkv][hd] each
+  void* vscr;
   float* logits;
   void* vws;
   int32_t* dints;
@@ -192,7 +203,7 @@ struct tri_session {
 namespace {
 
 struct SessionLayout {
-  size_t k, v, rope, x, y, y2, q, a, part, part2, attn, logits, vws, ints, conf, total;
+  size_t k, v, rope, x, y, y2, q, a, part, part2, attn, kscr, vscr, logits, vws, ints, conf, total;
   size_t part_floats, part2_floats, attn_bytes, nints;
   size_t o_meta0, o_meta1, o_out_tok, o_out_commit, o_status, o_accept, o_committed, o_kvlen, o_drafts, o_ars;
   int ctx, kv_split;
@@ -213,7 +224,10 @@ SessionLayout session_layout(const tri_model* m, int max_batch, int max_ctx, int
                               slotsN(m->p_gu, 2 * d.d_ffn, 0), slotsN(m->p_down, d.d_model, 0)});
   S.part_floats = pf * max_rows;
   S.part2_floats = d.lora_rank > 0 ? (size_t)m->p_la.S * d.lora_rank * max_rows : 64;
-  S.attn_bytes = attn_ws_bytes(max_rows, d.n_q_heads, d.head_dim, S.ctx, S.kv_split);
+  // a forward with quadratic-speculation blocks writes split partials even
+  // when its keys fit one split
+  S.attn_bytes = std::max(attn_ws_bytes(max_rows, d.n_q_heads, d.head_dim, S.ctx, S.kv_split),
+                          (size_t)max_rows * d.n_q_heads * (d.head_dim + 2) * sizeof(float) + 256);
   const MetaLayout ML = meta_layout(max_rows, max_batch);
   size_t o = 0;
   auto take = [&](size_t n) {
@@ -249,6 +263,8 @@ SessionLayout session_layout(const tri_model* m, int max_batch, int max_ctx, int
   S.part = region(S.part_floats * sizeof(float));
   S.part2 = region(S.part2_floats * sizeof(float));
   S.attn = region(S.attn_bytes);
+  S.kscr = region((size_t)max_rows * d.n_kv_heads * d.head_dim * m->esz);
+  S.vscr = region((size_t)max_rows * d.n_kv_heads * d.head_dim * m->esz);
   S.logits = region((size_t)max_rows * d.vocab * sizeof(float));
   S.vws = region(vocab_ws_bytes(max_rows, d.vocab));
   S.ints = region(S.nints * sizeof(int32_t));
@@ -309,6 +325,7 @@ int stage_meta(tri_session* s, int which, const HostRows& R, const std::vector<i
   memcpy(h.seq, R.seq.data(), n * 4);
   memcpy(h.lora, R.lora.data(), n * 4);
   memcpy(h.kind, R.kind.data(), n * 4);
+  if (R.blk_len > 0) memcpy(h.blk, R.blk.data(), n * 4);
   memcpy(h.seq_start, R.seq_start.data(), R.seq_start.size() * 4);
   memcpy(h.slot_seq, R.slot_seq.data(), R.slot_seq.size() * 4);
   if (!R.block_start.empty()) memcpy(h.block_start, R.block_start.data(), R.block_start.size() * 4);
@@ -372,7 +389,7 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
       // bf16 sessions keep V in the attention's fp16 form (same bits, staged without conversion)
       HIPCHK(launch_rope_kv(dt, s->part, gemm_out_slots(dt, m->p_qkv, n, m->qkv_n, D, inv), stride, n, hq, hkv, hd,
                             dm.seq, dm.pos, s->rope, s->qbuf, kc, vc, s->ctx, s->css, s->st, dt == TRI_BF16,
-                            vsat));
+                            vsat, R.blk_len > 0 ? dm.blk : nullptr, s->kscr, s->vscr));
     }
     {
       AttnLaunch a;
@@ -401,6 +418,12 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
       a.out = s->abuf;
       a.part = static_cast<float*>(s->attn_ws);
       a.v_f16 = dt == TRI_BF16;
+      if (R.blk_len > 0) {
+        a.row_blk = dm.blk;
+        a.k_scr = s->kscr;
+        a.v_scr = s->vscr;
+        a.blk_len = R.blk_len;
+      }
       PROF(PROF_ATTN, launch_attn(dt, a, s->st));
     }
     const size_t ostride = (size_t)n * D;
@@ -503,7 +526,14 @@ void pending_rows(const Seq& S, int seq, HostRows& R, int last_kind) {
 }
 
 // ------------------------------------------------------------------ modes
+// Carried quadratic-speculation drafts belong to the state they were drafted
+// from: any other step, prefill, append or rollback of the sequence drops them.
+void drop_qdrafts(tri_session* s, const std::vector<int>& act) {
+  for (int b : act) s->seqs[b].qdrafts.clear();
+}
+
 int step_ar(tri_session* s, const std::vector<int>& act, int stride, int32_t* out_tokens, tri_seq_stats* st) {
+  drop_qdrafts(s, act);
   HostRows R;
   std::vector<int> last_row(act.size());
   for (size_t j = 0; j < act.size(); ++j) {
@@ -537,6 +567,7 @@ int step_ar(tri_session* s, const std::vector<int>& act, int stride, int32_t* ou
 // order (optional): the positions of each block in the order they were committed.
 int step_diffusion(tri_session* s, const std::vector<int>& act, int B, float tau, int stride, int32_t* out_tokens,
                    tri_seq_stats* st, std::vector<std::vector<int>>* order = nullptr, bool use_sched = true) {
+  drop_qdrafts(s, act);
   const int mask = s->m->d.vocab;
   const size_t na = act.size();
   std::vector<std::vector<int32_t>> y(na, std::vector<int32_t>(B, mask));
@@ -682,6 +713,7 @@ int sol_parallel(tri_session* s, const std::vector<int>& act, int B, const std::
 // into the verify metadata), so the two forwards run back to back.
 int step_round(tri_session* s, const std::vector<int>& act, const std::vector<char>& spec, int k, int stride,
                int32_t* out_tokens, tri_seq_stats* st) {
+  drop_qdrafts(s, act);
   const int mask = s->m->d.vocab;
   const size_t na = act.size();
   int nv = 0;
@@ -811,6 +843,80 @@ int step_round(tri_session* s, const std::vector<int>& act, const std::vector<ch
 int step_selfspec(tri_session* s, const std::vector<int>& act, int k, int stride, int32_t* out_tokens,
                   tri_seq_stats* st) {
   return step_round(s, act, std::vector<char>(act.size(), 1), k, stride, out_tokens, st);
+}
+
+// Quadratic self-speculation ([Notes §8.1]; [Blog], performance highlights;
+// reading R24): one forward per round.  Per sequence, its pending rows and
+// the drafts carried from the previous round are clean causal rows (the AR
+// pathway: their greedy tokens g_0..g_n verify the drafts), followed by one
+// block of k+1 [MASK] rows at L+b .. L+b+k for every possible accept length
+// b = 0..n (the diffusion pathway drafts every outcome's continuation; LoRA
+// rows): a block row attends to the cache keys [0, L+b) and to its own
+// block.  a = the accept length; g_0..g_a are committed, the K/V of the
+// pending rows and d_0..d_{a-1} stay, g_a is the new pending token, and
+// block a's greedy tokens at L+a+1 .. L+a+k are the next drafts.  Without
+// carried drafts (the first round, or after any other step) the forward is
+// the pending rows and block 0, and commits g_0.  The accept length is taken
+// on the host from the tokens the sampler returns.
+int step_quad(tri_session* s, const std::vector<int>& act, int k, int stride, int32_t* out_tokens,
+              tri_seq_stats* st) {
+  const int mask = s->m->d.vocab;
+  const int lora = s->lora_on ? 1 : 0;
+  const size_t na = act.size();
+  HostRows R;
+  R.blk_len = k + 1;
+  std::vector<int> g0row(na), blk0(na);
+  std::vector<std::vector<int32_t>> drafts(na);
+  for (size_t j = 0; j < na; ++j) {
+    Seq& S = s->seqs[act[j]];
+    const int L = (int)S.tokens.size();
+    drafts[j] = S.qdrafts;
+    if (S.a_star >= 0 && !drafts[j].empty()) {  // controlled acceptance (benchmark hook)
+      for (int i = 0; i < (int)drafts[j].size(); ++i) {
+        int32_t t = L + i < (int)S.ref.size() ? S.ref[L + i] : 0;
+        if (i == S.a_star) t = (t + 1) % mask;
+        drafts[j][i] = t;
+      }
+    }
+    pending_rows(S, act[j], R, 1);
+    g0row[j] = R.n() - 1;
+    const int nd = (int)drafts[j].size();
+    for (int i = 0; i < nd; ++i) R.add(drafts[j][i], L + i, L + i + 1, act[j], 0, 1);
+    blk0[j] = R.n();
+    for (int b = 0; b <= nd; ++b) {
+      const int first = R.n();
+      for (int i = 0; i <= k; ++i) R.add(mask, L + b + i, L + b, act[j], lora, 1, first);
+    }
+    R.close_slot(act[j]);
+  }
+  int rc = stage_meta(s, 0, R, {}, {});
+  if (!rc) rc = upload_meta(s, 0);
+  if (!rc) rc = forward(s, 0, R, s->logits);
+  if (!rc) rc = sample(s, 0, R, s->logits, 0.f, 0);
+  if (!rc) rc = d2h_ints(s, s->o_out_tok, R.n());
+  if (!rc) rc = d2h_ints(s, s->o_status, 4);
+  if (rc) return rc;
+  HIPCHK(hipStreamSynchronize(s->st));
+  rc = check_status(s, 1, "a quadratic self-speculation round");
+  if (rc) return rc;
+  for (size_t j = 0; j < na; ++j) {
+    Seq& S = s->seqs[act[j]];
+    const int L = (int)S.tokens.size();
+    const int nd = (int)drafts[j].size();
+    const int32_t* g = s->hints + s->o_out_tok + g0row[j];
+    int a = 0;
+    while (a < nd && drafts[j][a] == g[a]) ++a;
+    for (int i = 0; i <= a; ++i) {
+      S.tokens.push_back(g[i]);
+      out_tokens[(size_t)act[j] * stride + i] = g[i];
+    }
+    S.kv_len = L + a;
+    S.written_hi = L + a;
+    const int32_t* nb = s->hints + s->o_out_tok + blk0[j] + a * (k + 1) + 1;
+    S.qdrafts.assign(nb, nb + k);
+    if (st) st[act[j]] = tri_seq_stats{a + 1, 1, a, 0};
+  }
+  return TRI_OK;
 }
 
 // Mode choice by concurrency ([Notes] §2 mode table and §11; [Digest], Limitations): forward cost from
@@ -1050,6 +1156,8 @@ int tri_session_create(const tri_model* m, int max_batch, int max_ctx, int max_r
   s->part = reinterpret_cast<float*>(base + S.part);
   s->part2 = reinterpret_cast<float*>(base + S.part2);
   s->attn_ws = base + S.attn;
+  s->kscr = base + S.kscr;
+  s->vscr = base + S.vscr;
   s->logits = reinterpret_cast<float*>(base + S.logits);
   s->vws = base + S.vws;
   s->dints = reinterpret_cast<int32_t*>(base + S.ints);
@@ -1140,6 +1248,7 @@ int tri_prefill(tri_session* s, int seq, const int32_t* tokens, int n) {
   S.a_star = -1;
   S.ref.clear();
   S.sched.clear();
+  S.qdrafts.clear();
   for (int b = 0; b < n - 1; b += s->max_rows) {
     const int e = std::min(n - 1, b + s->max_rows);
     HostRows R;
@@ -1172,8 +1281,10 @@ int tri_prefill(tri_session* s, int seq, const int32_t* tokens, int n) {
 int tri_decode_step(tri_session* s, int mode, int block, float threshold, int32_t* out_tokens,
                     tri_seq_stats* out_stats) {
   if (!s || !out_tokens) return fail(TRI_EINVAL, "null argument");
-  if (mode != TRI_AR && mode != TRI_DIFFUSION && mode != TRI_SELFSPEC) return fail(TRI_EINVAL, "bad mode %d", mode);
+  if (mode != TRI_AR && mode != TRI_DIFFUSION && mode != TRI_SELFSPEC && mode != TRI_QUADSPEC)
+    return fail(TRI_EINVAL, "bad mode %d", mode);
   if (block < 1 || block > 64) return fail(TRI_EINVAL, "block %d outside [1, 64]", block);
+  if (mode == TRI_QUADSPEC && block > 63) return fail(TRI_EINVAL, "quadratic self-speculation needs k <= 63");
   if (mode == TRI_DIFFUSION && !(threshold >= 0.f && threshold <= 1.f))
     return fail(TRI_EINVAL, "threshold must be in [0, 1]");
   std::vector<int> act;
@@ -1184,9 +1295,16 @@ int tri_decode_step(tri_session* s, int mode, int block, float threshold, int32_
     const int L = (int)S.tokens.size();
     const int pend = L - S.kv_len;
     if (pend < 1) return fail(TRI_ESTATE, "sequence %d has no pending token (kv_len %d, L %d)", b, S.kv_len, L);
-    const int need = mode == TRI_AR ? L + 1 : (mode == TRI_DIFFUSION ? L + block : L + block + 1);
+    const int nd = mode == TRI_QUADSPEC ? (int)S.qdrafts.size() : 0;  // carried drafts
+    const int need = mode == TRI_AR ? L + 1
+                     : mode == TRI_DIFFUSION ? L + block
+                     : mode == TRI_SELFSPEC ? L + block + 1
+                                            : L + nd + block + 1;  // the last block's last row
     if (need > s->max_ctx) return fail(TRI_ECAPACITY, "sequence %d would pass max_ctx %d", b, s->max_ctx);
-    const int r = mode == TRI_AR ? pend : (mode == TRI_DIFFUSION ? pend + block : std::max(pend + block, block));
+    const int r = mode == TRI_AR ? pend
+                  : mode == TRI_DIFFUSION ? pend + block
+                  : mode == TRI_SELFSPEC ? std::max(pend + block, block)
+                                         : pend + nd + (nd + 1) * (block + 1);
     rows += r;
     act.push_back(b);
   }
@@ -1200,6 +1318,7 @@ int tri_decode_step(tri_session* s, int mode, int block, float threshold, int32_
   switch (mode) {
     case TRI_AR: return step_ar(s, act, stride, out_tokens, out_stats);
     case TRI_DIFFUSION: return step_diffusion(s, act, block, threshold, stride, out_tokens, out_stats);
+    case TRI_QUADSPEC: return step_quad(s, act, block, stride, out_tokens, out_stats);
     default: return step_selfspec(s, act, block, stride, out_tokens, out_stats);
   }
 }
@@ -1364,6 +1483,7 @@ int kv_append(tri_session* s, int seq, int n) {
     return fail(TRI_ESTATE, "append of %d rows passes the committed (%d) or written (%d) rows", n, (int)S.tokens.size(),
                 S.written_hi);
   S.kv_len += n;
+  S.qdrafts.clear();
   return TRI_OK;
 }
 
@@ -1375,6 +1495,7 @@ int kv_rollback(tri_session* s, int seq, int n) {
   if (n > S.kv_len) return fail(TRI_ESTATE, "rollback of %d rows with kv_len %d", n, S.kv_len);
   S.kv_len -= n;
   S.written_hi = S.kv_len;
+  S.qdrafts.clear();
   return TRI_OK;
 }
 

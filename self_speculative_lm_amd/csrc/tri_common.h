@@ -150,6 +150,9 @@ int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invar
 // h = bf16(silu(gate) * up) [M][N/2] instead of float32 slots, bit-identical
 // to the slots followed by the SwiGLU kernel.
 bool gemm_swiglu_fused(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant);
+// One past the highest packed W element launch_gemm's kernel reads (host
+// evaluation of the kernels' address arithmetic over the launch grid).
+size_t gemm_w_reach(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant);
 hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, int N, const GemmPlan& plan,
                        float* P, size_t slot_stride, bool invariant, hipStream_t st, void* swiglu_out = nullptr);
 
@@ -167,6 +170,14 @@ struct AttnLaunch {
   void* out;
   float* part;  // split partials
   bool v_f16 = false;  // bf16: the V cache holds the fp16 form written by launch_rope_kv(v_f16)
+  // Quadratic-speculation blocks: a row with row_blk[r] >= 0 also attends to
+  // the blk_len keys of rows [row_blk[r], row_blk[r] + blk_len) of the row
+  // scratch (k_scr, v_scr [rows][hkv][hd], written by launch_rope_kv), after
+  // the cache keys [0, row_hi[r]).  NULL: no block rows.
+  const int32_t* row_blk = nullptr;
+  const void* k_scr = nullptr;
+  const void* v_scr = nullptr;
+  int blk_len = 0;
 };
 int attn_pick_split(int max_ctx, int n_seq, int hq, int hkv);
 int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int hkv);
@@ -178,11 +189,15 @@ hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, 
                         float* x, hipStream_t st);
 hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, size_t slot_stride,
                              int rows, int d, const float* g, float eps, void* y, hipStream_t st);
-// vsat: set to 1 when a V value saturates its fp16 form (v_f16).
+// vsat: set to 1 when a V value saturates its fp16 form (v_f16).  row_blk
+// (optional, device int32 [rows]): rows with row_blk[r] >= 0 belong to a
+// quadratic-speculation block and write k, v to kscr / vscr [rows][hkv][hd]
+// (model storage type) instead of the cache.
 hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
                           int hq, int hkv, int hd, const int32_t* row_seq, const int32_t* row_pos,
                           const float* rope, void* qout, void* kc, void* vc, int ctx,
-                          size_t cache_seq_stride, hipStream_t st, bool v_f16 = false, int32_t* vsat = nullptr);
+                          size_t cache_seq_stride, hipStream_t st, bool v_f16 = false, int32_t* vsat = nullptr,
+                          const int32_t* row_blk = nullptr, void* kscr = nullptr, void* vscr = nullptr);
 hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t slot_stride, int rows,
                          int ffn, void* h, hipStream_t st);
 hipError_t launch_lora_mid(int dtype, const float* P, int nslots, size_t slot_stride, int rows,

@@ -161,7 +161,7 @@ def attention_alone(args):
     hq, hkv, hd, nb = 32, 8, 128, 32
     g = torch.Generator(device=dev).manual_seed(3)
     clocks0 = gpu_clocks()
-    for P in (512, 2048, 8192, 32768):
+    for P in args.attn_prefix or (512, 2048, 8192, 32768):
         for b in (1, 8):
             L = P + nb
             ctx = (L + 63) // 64 * 64
@@ -638,6 +638,8 @@ def main():
     ap.add_argument("--no-replay", action="store_true")
     ap.add_argument("--attn", action="store_true",
                     help="time block_causal_attn alone at the attention-only shapes instead of the decode round")
+    ap.add_argument("--attn-prefix", type=int, nargs="*", default=None,
+                    help="with --attn: only these prefix lengths (default 512 2048 8192 32768)")
     ap.add_argument("--attn-splits", action="store_true",
                     help="block_causal_attn alone at 4K..32K keys with every key split forced")
     ap.add_argument("--concurrency", action="store_true",

@@ -325,6 +325,20 @@ int block_causal_attn(const void* q, const void* k_cache, const void* v_cache, i
                       float scale, int dtype, int kv_split, void* out, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* block_causal_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the split partials in a
+ * static device scratch of 32 MiB that the library holds on every GPU it
+ * runs on.  No workspace argument; calls no hipMalloc/hipFree.  kv_split 0
+ * picks the split as block_causal_attn does.  TRI_ECAPACITY when the
+ * partials (block_causal_attn_ws_bytes) exceed 32 MiB.  Calls on one GPU
+ * share its scratch: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller. */
+int block_causal_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, int n_seq,
+                              const int32_t* seq_start, const int32_t* row_hi, int rows,
+                              int max_rows_per_seq, int max_hi, int hq, int hkv, int hd, int ctx,
+                              float scale, int dtype, int kv_split, void* out, void* stream);
+
 /* Vocabulary reduction and commit decision [Notes §5.2, §5.3; Blog, FastDiffuser].
  * For every row with row_kind != 0: out_tok = argmax of logits (lowest id on
  * ties), out_conf = max softmax probability = 1/sum_j exp(l_j - max).

@@ -15,7 +15,7 @@ import numpy as np
 from ._lib import (TRI_AR, TRI_BF16, TRI_BF16_V16, TRI_DIFFUSION, TRI_F32, TRI_QUADSPEC, TRI_SELFSPEC, ModelDesc, SeqStats, TriError,  # noqa: F401
                    check, lib)
 
-__all__ = ["Model", "Session", "block_causal_attn", "sample_commit", "verify_accept", "weight_names", "choose_modes",
+__all__ = ["Model", "Session", "block_causal_attn", "block_causal_attn_noalloc", "sample_commit", "verify_accept", "weight_names", "choose_modes",
            "TriError", "TRI_AR", "TRI_DIFFUSION", "TRI_SELFSPEC", "TRI_QUADSPEC", "TRI_F32", "TRI_BF16", "TRI_BF16_V16"]
 
 
@@ -280,6 +280,24 @@ def block_causal_attn(q, k_cache, v_cache, seq_start, row_hi, out, scale: float,
     check(lib().block_causal_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), n_seq, _ptr(seq_start), _ptr(row_hi), rows,
                                   max_rows_per_seq, max_hi, hq, hkv, hd, ctx, float(scale), dtype, kv_split,
                                   _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def block_causal_attn_noalloc(q, k_cache, v_cache, seq_start, row_hi, out, scale: float, *, max_rows_per_seq: int,
+                              max_hi: int, kv_split: int = 0, dtype: Optional[int] = None, stream=None):
+    """block_causal_attn with the split partials in the library's static device
+    scratch (no workspace; for callers that cannot allocate)."""
+    torch = _torch()
+    rows, hq, hd = q.shape
+    n_seq, hkv, ctx, _ = k_cache.shape
+    if dtype is None:
+        if q.dtype == torch.bfloat16:
+            dtype = TRI_BF16_V16 if v_cache.dtype == torch.float16 else TRI_BF16
+        else:
+            dtype = TRI_F32
+    check(lib().block_causal_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), n_seq, _ptr(seq_start),
+                                          _ptr(row_hi), rows, max_rows_per_seq, max_hi, hq, hkv, hd, ctx, float(scale),
+                                          dtype, kv_split, _ptr(out), _stream(stream)))
     return out
 
 

@@ -67,6 +67,7 @@ SIGNATURES = {
     "tri_profile_read": (I, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]),
     "block_causal_attn_ws_bytes": (I, [I, I, I, I, I, ctypes.POINTER(SZ)]),
     "block_causal_attn": (I, [P, P, P, I, P, P, I, I, I, I, I, I, I, F, I, I, P, P, SZ, P]),
+    "block_causal_attn_noalloc": (I, [P, P, P, I, P, P, I, I, I, I, I, I, I, F, I, I, P, P]),
     "sample_commit_ws_bytes": (I, [I, I, ctypes.POINTER(SZ)]),
     "sample_commit": (I, [P, I, I, P, P, I, F, P, P, P, P, P, SZ, P]),
     "verify_accept": (I, [P, P, I, I, P, P, P, P]),

@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1700,6 +1701,52 @@ int block_causal_attn(const void* q, const void* k_cache, const void* v_cache, i
   a.v_f16 = v16;
   HIPCHK(launch_attn(dtype, a, static_cast<hipStream_t>(stream)));
   return TRI_OK;
+}
+
+// ------------------------------------------------- allocation-free variant
+// block_causal_attn without a workspace argument, for callers that cannot
+// allocate device memory: the split partials live in this file-scope device
+// array.  Every GPU the library runs on holds its own copy for the life of
+// the process; host code uses the address hipGetSymbolAddress returns for the
+// current device (kept per device), never the array's name.
+constexpr size_t ATTN_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) char attn_scratch[ATTN_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(TRI_EINVAL, "device %d beyond the %d the library tracks", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(attn_scratch)));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TRI_OK;
+}
+}  // namespace
+
+int block_causal_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, int n_seq,
+                              const int32_t* seq_start, const int32_t* row_hi, int rows, int max_rows_per_seq,
+                              int max_hi, int hq, int hkv, int hd, int ctx, float scale, int dtype, int kv_split,
+                              void* out, void* stream) {
+  if (rows < 0 || hq <= 0 || hd <= 0 || max_hi < 0 || kv_split < 0 || kv_split % 64) return fail(TRI_EINVAL, "bad shape");
+  const int split = kv_split == 0 && hkv > 0 ? attn_pick_split_launch(max_hi, n_seq, max_rows_per_seq, hq, hkv) : kv_split;
+  const size_t need = attn_ws_bytes(rows, hq, hd, max_hi, split);
+  if (need > ATTN_SCRATCH_BYTES)
+    return fail(TRI_ECAPACITY, "split partials need %zu bytes, the static scratch holds %zu (fewer rows or longer kv_split)",
+                need, ATTN_SCRATCH_BYTES);
+  void* ws = nullptr;
+  int rc = scratch_for_current_device(&ws);
+  if (rc) return rc;
+  return block_causal_attn(q, k_cache, v_cache, n_seq, seq_start, row_hi, rows, max_rows_per_seq, max_hi, hq, hkv, hd,
+                           ctx, scale, dtype, split, out, ws, ATTN_SCRATCH_BYTES, stream);
 }
 
 int sample_commit_ws_bytes(int rows, int vocab, size_t* bytes) {

@@ -659,12 +659,32 @@ int attn_pick_split(int max_ctx, int n_seq, int hq, int hkv) {
   int s = 128;
   const double lim = (double)max_ctx / 16.0;
   while (s < 2048 && 2.0 * s <= lim) s *= 2;
+  // Long-context sessions (their decode forwards do run near capacity): a
+  // workgroup holds a CU's LDS, so a launch of more than 256 workgroups runs
+  // in two rounds, the second as long as the first.  Take the smallest
+  // multiple of 64 keys, up to twice the split above, that keeps a
+  // full-capacity launch of 33-row blocks in one round (for example the
+  // 14B-class heads, 40q/8kv with two query groups per split, behind a 16K
+  // prefix: 16 splits of 1088 keys, 256 workgroups, instead of 17 of 1024).
+  if (max_ctx >= 8192 && hkv > 0) {
+    const int qtiles = (33 * (hq / hkv) + 15) / 16;
+    int qw, qt;
+    attn_shape(qtiles, max_ctx, &qw, &qt);
+    const long per_split = (long)((qtiles + qw * qt - 1) / (qw * qt)) * hkv;
+    const long ns_max = 256 / per_split;
+    if (ns_max >= 1) {
+      const int s2 = (int)(((max_ctx + ns_max - 1) / ns_max + 63) / 64 * 64);
+      if (s2 > s && s2 <= 2 * s) s = s2;
+    }
+  }
   return s;
 }
 
 int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int hkv) {
-  // Keys per split for one launch (the C-ABI's kv_split = 0): the power of two
-  // in [128, 4096] with the lowest modelled time.  Model, fitted to MI355X
+  // Keys per split for one launch (the C-ABI's kv_split = 0): the multiple of
+  // 64 in [128, 4096] with the lowest modelled time (multiples of 64, not
+  // only powers of two, so that a launch can fill whole rounds of 256
+  // workgroups; ties go to the shorter split).  Model, fitted to MI355X
   // measurements at 32q/8kv heads, 32-row blocks, prefixes 512..32K, 1 and 8
   // sequences: a workgroup costs 4 us plus 1.8 us per 128 keys it walks (two
   // key groups of 64-key tiles), workgroups run one per CU in waves of 256,
@@ -679,7 +699,7 @@ int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int 
   const double fixed = qt == 2 ? 13.0 : 4.0, per128 = qt == 2 ? 2.8 : 1.8, combine = qt == 2 ? 0.0 : 4.0;
   int best = 128;
   double bt = 1e30;
-  for (int sp = 128; sp <= 4096; sp *= 2) {
+  for (int sp = 128; sp <= 4096; sp += 64) {
     const long ns = std::max(1, (max_hi + sp - 1) / sp);
     const long nwg = ns * qg * std::max(1, n_seq) * std::max(1, hkv);
     const double t =

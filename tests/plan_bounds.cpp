@@ -1,9 +1,13 @@
-// Host check of the GEMM launches' weight reads: for every projection plan the
-// library builds for the named model shapes, and row counts covering the
-// decode kernel (1..64) and the large-M kernel's forms (tall and square, one
-// slot and chained), the highest packed weight element a launch reads must lie
-// inside the packed matrix.  Prints one line per shape and exits non-zero on
-// a violation.
+// Host checks of launch plans.
+// GEMM: for every projection plan the library builds for the named model
+// shapes, and row counts covering the decode kernel (1..64) and the large-M
+// kernel's forms (tall and square, one slot and chained), the highest packed
+// weight element a launch reads must lie inside the packed matrix.
+// Attention splits: every split the session rule or the per-launch model picks
+// is a multiple of 64 keys in [128, 4096], and a long-context session (8K keys
+// or more) keeps a full-capacity launch of 33-row blocks within one round of
+// 256 workgroups whenever the rule's bound allows it.
+// Prints one line per check group and exits non-zero on a violation.
 #include <cstdio>
 #include <cstdlib>
 
@@ -54,6 +58,40 @@ int main() {
     }
     printf("%s: %ld launches checked\n", s.name, checks);
   }
+  long splits = 0;
+  const int heads[][2] = {{32, 8}, {40, 8}, {4, 2}, {5, 1}, {64, 8}};
+  for (const auto& h : heads) {
+    const int hq = h[0], hkv = h[1], G = hq / hkv;
+    for (int ctx = 64; ctx <= 131072; ctx += ctx < 4096 ? 64 : 1024)
+      for (int n_seq : {1, 2, 8, 16}) {
+        const int sp = attn_pick_split(ctx, n_seq, hq, hkv);
+        ++splits;
+        if (sp % 64 || sp < 128 || sp > 4096) {
+          printf("session split %d for ctx %d, %d sequences, %dq/%dkv\n", sp, ctx, n_seq, hq, hkv);
+          ++bad;
+        }
+        if (n_seq == 1 && ctx >= 8192) {
+          const int qtiles = (33 * G + 15) / 16;
+          const int per_wg = qtiles >= 8 ? 8 : 4;  // query tiles per workgroup beyond 4K keys
+          const long wgs = (long)((ctx + sp - 1) / sp) * ((qtiles + per_wg - 1) / per_wg) * hkv;
+          int pow2 = 128;
+          while (pow2 < 2048 && 2.0 * pow2 <= ctx / 16.0) pow2 *= 2;
+          const long per_split = (long)((qtiles + per_wg - 1) / per_wg) * hkv;
+          const long ns_max = 256 / per_split;
+          const bool fits = ns_max >= 1 && ((ctx + ns_max - 1) / ns_max + 63) / 64 * 64 <= 2 * pow2;
+          if (fits && wgs > 256) {
+            printf("session split %d for ctx %d, %dq/%dkv: %ld workgroups at capacity\n", sp, ctx, hq, hkv, wgs);
+            ++bad;
+          }
+        }
+        const int sl = attn_pick_split_launch(ctx, n_seq, 32, hq, hkv);
+        if (sl % 64 || sl < 128 || sl > 4096) {
+          printf("launch split %d for %d keys, %d sequences, %dq/%dkv\n", sl, ctx, n_seq, hq, hkv);
+          ++bad;
+        }
+      }
+  }
+  printf("attention: %ld split choices checked\n", splits);
   printf(bad ? "FAIL %d\n" : "OK\n", bad);
   return bad ? 1 : 0;
 }

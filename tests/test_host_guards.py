@@ -2,7 +2,10 @@
 
 * every GEMM launch the library makes for the model shapes reads its packed
   weights inside their bounds (tests/plan_bounds.cpp evaluates the kernels'
-  address arithmetic over each launch grid on the host);
+  address arithmetic over each launch grid on the host), and every attention
+  key split the library picks is a whole number of 64-key tiles in range,
+  with long-context sessions fitting a full-capacity launch in one round of
+  workgroups;
 * the runtime's host code built with AddressSanitizer and
   UndefinedBehaviorSanitizer passes the host-only C-ABI tests (argument
   validation, model and session sizing, the mode choice by concurrency)."""
@@ -28,7 +31,7 @@ def _lib():
     return _lib.LIB_PATH
 
 
-def test_every_gemm_launch_reads_inside_its_packed_weights(tmp_path):
+def test_launch_plans_stay_inside_their_bounds(tmp_path):
     from self_speculative_lm_amd.build import hipcc
     lib = _lib()
     exe = str(tmp_path / "plan_bounds")

@@ -554,16 +554,17 @@ def diffusion_sweep(args):
 
     base = {"metric": "8B-class diffusion mode, block 32, 1024-token prompt, 512 new tokens per sequence",
             "data": "synthetic (seeded random-init weights, uniform random prompts)"}
-    for n in (1, 4, 16):
+    for n in args.diffusion_batch or (1, 4, 16):
         for tau in (0.5, 0.7, 0.9):
             res = dict(base, batch=n, threshold=tau, **run(n, tm.TRI_DIFFUSION, tau))
             print(json.dumps(res), flush=True)
         res = dict(base, batch=n, threshold="controlled commit schedule, mean 2.6 per forward",
                    **run(n, tm.TRI_DIFFUSION, 0.9, controlled=True))
         print(json.dumps(res), flush=True)
-    res = dict(base, metric="8B-class AR mode, 1024-token prompt, 512 new tokens per sequence", batch=16,
-               **run(16, tm.TRI_AR))
-    print(json.dumps(res), flush=True)
+    if not args.diffusion_batch:
+        res = dict(base, metric="8B-class AR mode, 1024-token prompt, 512 new tokens per sequence", batch=16,
+                   **run(16, tm.TRI_AR))
+        print(json.dumps(res), flush=True)
 
 
 def long_prefix_14b(args):
@@ -648,6 +649,8 @@ def main():
                     help="speed-of-light analysis (serial denoising + parallel pass) at 1 and 8 sequences")
     ap.add_argument("--diffusion", action="store_true",
                     help="8B-class diffusion mode at 1/4/16 sequences and thresholds 0.5/0.7/0.9, plus AR at 16")
+    ap.add_argument("--diffusion-batch", type=int, nargs="*", default=None,
+                    help="with --diffusion: only these sequence counts (default 1 4 16, then AR at 16)")
     ap.add_argument("--quad", action="store_true",
                     help="quadratic self-speculation on the 8B-class model at k = 4..32, next to linear")
     ap.add_argument("--long14b", action="store_true",

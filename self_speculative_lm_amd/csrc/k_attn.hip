@@ -681,36 +681,45 @@ int attn_pick_split(int max_ctx, int n_seq, int hq, int hkv) {
 }
 
 int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int hkv) {
-  // Keys per split for one launch (the C-ABI's kv_split = 0): the multiple of
-  // 64 in [128, 4096] with the lowest modelled time (multiples of 64, not
-  // only powers of two, so that a launch can fill whole rounds of 256
-  // workgroups; ties go to the shorter split).  Model, fitted to MI355X
-  // measurements at 32q/8kv heads, 32-row blocks, prefixes 512..32K, 1 and 8
-  // sequences: a workgroup costs 4 us plus 1.8 us per 128 keys it walks (two
-  // key groups of 64-key tiles), workgroups run one per CU in waves of 256,
-  // and more than one split adds a 4 us combine.  Workgroups of two query
-  // tiles per wave (long prefixes) were fitted separately, at prefixes 4K..32K:
-  // 13 us plus 2.8 us per 128 keys, no measurable combine term.
+  // Keys per split for one launch (the C-ABI's kv_split = 0): the power of two
+  // in [128, 4096] with the lowest modelled time, or the multiple of 64 with
+  // the lowest modelled time when that is at least 10% lower (a split that
+  // fills whole rounds of 256 workgroups; the margin keeps near-ties, where
+  // the model's error decides, on the measured powers of two: at 16 sequences
+  // x 1.7K keys its 2% edge for 832-key splits was a 7% loss per forward).
+  // Model, fitted to MI355X measurements at 32q/8kv heads, 32-row blocks,
+  // prefixes 512..32K, 1 and 8 sequences: a workgroup costs 4 us plus 1.8 us
+  // per 128 keys it walks (two key groups of 64-key tiles), workgroups run one
+  // per CU in waves of 256, and more than one split adds a 4 us combine.
+  // Workgroups of two query tiles per wave (long prefixes) were fitted
+  // separately, at prefixes 4K..32K: 13 us plus 2.8 us per 128 keys, no
+  // measurable combine term.
   const int G = hkv > 0 ? hq / hkv : 1;
   const int qtiles = std::max(1, (rows_per_seq * G + 15) / 16);
   int qw, qt;
   attn_shape(qtiles, max_hi, &qw, &qt);
   const long qg = (qtiles + qw * qt - 1) / (qw * qt);
   const double fixed = qt == 2 ? 13.0 : 4.0, per128 = qt == 2 ? 2.8 : 1.8, combine = qt == 2 ? 0.0 : 4.0;
-  int best = 128;
-  double bt = 1e30;
-  for (int sp = 128; sp <= 4096; sp += 64) {
+  auto model = [&](int sp) {
     const long ns = std::max(1, (max_hi + sp - 1) / sp);
     const long nwg = ns * qg * std::max(1, n_seq) * std::max(1, hkv);
-    const double t =
-        std::ceil(nwg / 256.0) * (fixed + per128 * std::ceil(std::min(sp, std::max(max_hi, 1)) / 128.0)) +
-        (ns > 1 ? combine : 0.0);
-    if (t < bt) {
-      bt = t;
-      best = sp;
+    return std::ceil(nwg / 256.0) * (fixed + per128 * std::ceil(std::min(sp, std::max(max_hi, 1)) / 128.0)) +
+           (ns > 1 ? combine : 0.0);
+  };
+  int best2 = 128, best64 = 128;
+  double t2 = 1e30, t64 = 1e30;
+  for (int sp = 128; sp <= 4096; sp += 64) {
+    const double t = model(sp);
+    if ((sp & (sp - 1)) == 0 && t < t2) {
+      t2 = t;
+      best2 = sp;
+    }
+    if (t < t64) {
+      t64 = t;
+      best64 = sp;
     }
   }
-  return best;
+  return t64 <= 0.9 * t2 ? best64 : best2;
 }
 
 size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split) {

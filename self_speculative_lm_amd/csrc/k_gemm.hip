@@ -515,10 +515,14 @@ hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, cons
 // from 256 rows for the others.
 bool gemm_use_big(int M, int N, int K) { return M > 64 && (M >= 256 || N >= 16384 || K >= 8192); }
 
-// Large-M form: 8 waves x 4 fragments (512 features) x 4 row tiles (64 rows),
-// 4 k-steps in flight; measured best for the 8B shapes at 256..2048 rows
-// (up to 40% of the bf16 MFMA peak on the down projection).
-constexpr int BIGM_MT = 4, BIGM_D = 4, BIGM_FPW = 4, BIGM_WAVES = 8;
+// Large-M form: 8 waves x 2 fragments (256 features) x 4 row tiles (64 rows),
+// 4 k-steps in flight.  Two fragments per wave keep a wave under 128 VGPRs,
+// so two workgroups share a CU (their 64 KB X tiles fit its LDS); with four
+// fragments (512 features, ~180 VGPRs) one workgroup ran per CU.  Measured
+// on MI355X: the 511-row prefill chunk 12.9 -> 11.9 ms, the 8B-class
+// diffusion forward at 16 sequences (512 rows) 16.5 -> 16.1 ms; four row
+// tiles of 128 rows or two of 32 were slower.
+constexpr int BIGM_MT = 4, BIGM_D = 4, BIGM_FPW = 2, BIGM_WAVES = 8;
 constexpr int BIGM_BPW = BIGM_WAVES * BIGM_FPW / 8;  // packed blocks per workgroup
 // Tall form for 65..128 rows: one 128-row tile (8 row tiles) x 1 fragment
 // per wave, so W is streamed once for all the rows instead of once per

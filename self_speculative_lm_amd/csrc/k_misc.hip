@@ -5,6 +5,8 @@
 // other rows share the launch.
 #include <math.h>
 
+#include <algorithm>
+
 #include "tri_common.h"
 
 namespace tri {
@@ -40,13 +42,26 @@ __device__ __forceinline__ f32x4 slot_sum4(const float* P, int nslots, size_t st
 
 // x[r] = E[tok[r]]; an id outside [0, n_emb) (e.g. the -1 the sampler writes
 // for a row with non-finite logits) gives a zero row instead of a stray read.
+// Four columns per thread (d % 4 == 0), all of a row's loads issued at once.
 template <typename T>
-__global__ void embed_kernel(const int32_t* tok, const T* E, int n_emb, int d, float* x) {
+__global__ __launch_bounds__(1024) void embed_kernel(const int32_t* tok, const T* E, int n_emb, int d, float* x) {
   const int r = blockIdx.x;
   const int t = tok[r];
   const bool ok = t >= 0 && t < n_emb;
-  const size_t src = (size_t)(ok ? t : 0) * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) x[(size_t)r * d + c] = ok ? Elem<T>::load(E, src + c) : 0.f;
+  const T* src = E + (size_t)(ok ? t : 0) * d;
+  for (int c = 4 * (int)threadIdx.x; c < d; c += 4 * (int)blockDim.x) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      if constexpr (sizeof(T) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2*>(src + c);
+        v = f32x4{bf16_to_f32((bf16_t)(u.x & 0xffff)), bf16_to_f32((bf16_t)(u.x >> 16)),
+                  bf16_to_f32((bf16_t)(u.y & 0xffff)), bf16_to_f32((bf16_t)(u.y >> 16))};
+      } else {
+        v = *reinterpret_cast<const f32x4*>(src + c);
+      }
+    }
+    *reinterpret_cast<f32x4*>(x + (size_t)r * d + c) = v;
+  }
 }
 
 // x[r] += sum of slots; y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g   (RMSNorm).
@@ -468,10 +483,12 @@ __global__ void scatter_gather_kernel(const int32_t* src, const int32_t* sidx, c
 hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, int n_emb, int d, float* x,
                         hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (d % 4) return hipErrorInvalidValue;
+  const int threads = std::min(1024, (d / 4 + 63) / 64 * 64);
   TRI_DISPATCH(dtype,
-               hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(256), 0, st, tok,
+               hipLaunchKernelGGL(embed_kernel<float>, dim3(rows), dim3(threads), 0, st, tok,
                                   static_cast<const float*>(E), n_emb, d, x),
-               hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, tok,
+               hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(rows), dim3(threads), 0, st, tok,
                                   static_cast<const bf16_t*>(E), n_emb, d, x));
   return hipGetLastError();
 }

@@ -348,12 +348,13 @@ def quadratic_sweep(args):
 
 def concurrency_sweep(args):
     """Mixed AR / self-speculation steps on the 8B-class decoder at 1..64
-    sequences.  First the cost of one forward is measured at row counts from 1
-    to 64 x (k+1); then for each batch n the committed tokens/s of all-AR steps,
-    all-self-speculation steps and the per-sequence choice of tri_choose_modes
-    from that curve.  Acceptance is controlled per sequence: its drafts are the
-    GPU's own greedy continuation up to a*, with a mismatch forced at a*
-    (a* cycles over the sequences), so expected tokens per round = a* + 1."""
+    sequences.  First, for each batch n, the cost of one forward over the n
+    sequences at row counts from n to n x (k+1); then for each n the committed
+    tokens/s of all-AR steps, all-self-speculation steps and the per-sequence
+    choice of tri_choose_modes from that batch's curve.  Acceptance is
+    controlled per sequence: its drafts are the GPU's own greedy continuation
+    up to a*, with a mismatch forced at a* (a* cycles over the sequences), so
+    expected tokens per round = a* + 1."""
     import numpy as np
     import torch
     import seeded
@@ -379,23 +380,34 @@ def concurrency_sweep(args):
         torch.cuda.synchronize()
 
     prefill(nmax)
-    # cost curve: teacher-forced forwards (full lm_head and sampling) of R rows
-    # spread over the sequences as causal rows from each pending position
-    grid = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, nmax * (k + 1)]
-    grid_ms = []
-    for R in grid:
-        per = [R // nmax + (1 if i < R % nmax else 0) for i in range(min(R, nmax))]
-        seq = np.concatenate([np.full(c, i) for i, c in enumerate(per)]).astype(np.int32)
-        pos = np.concatenate([args.prompt - 1 + np.arange(c) for c in per]).astype(np.int32)
-        tok = np.array([prompts[i][j % args.prompt] for i, c in enumerate(per) for j in range(c)], dtype=np.int32)
-        ts = []
-        for rep in range(6):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            sess.forward(seq, tok, pos, pos + 1)
-            ts.append(time.perf_counter() - t0)
-        grid_ms.append(float(np.median(ts[1:])) * 1e3)
-        log(f"forward over {R} rows: {grid_ms[-1]:.2f} ms")
+    # points on both sides of the GEMM form switches (64 | 65 and 128 | 129 rows)
+    # so the interpolated cost sees their steps
+    base_grid = [1, 2, 4, 8, 16, 32, 64, 65, 96, 128, 129, 192, 256, 384, 512, 768, 1024, 1536]
+
+    def cost_curve(n):
+        """Teacher-forced forwards (full lm_head and sampling) of R rows spread
+        over n sequences as causal rows from each pending position, for R from
+        n (all AR) to n (k + 1) (all self-speculation): the attention reads the
+        same n caches whatever the mode mix, so the curve is taken per batch."""
+        grid = sorted({n, n * (k + 1)} | {g for g in base_grid if n < g < n * (k + 1)})
+        grid_ms = []
+        for R in grid:
+            per = [R // n + (1 if i < R % n else 0) for i in range(n)]
+            seq = np.concatenate([np.full(c, i) for i, c in enumerate(per)]).astype(np.int32)
+            pos = np.concatenate([args.prompt - 1 + np.arange(c) for c in per]).astype(np.int32)
+            tok = np.array([prompts[i][j % args.prompt] for i, c in enumerate(per) for j in range(c)], dtype=np.int32)
+            ts = []
+            for rep in range(6):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                sess.forward(seq, tok, pos, pos + 1)
+                ts.append(time.perf_counter() - t0)
+            grid_ms.append(float(np.median(ts[1:])) * 1e3)
+        log(f"{n} sequences: forward over " + ", ".join(f"{R} rows {m:.2f} ms" for R, m in zip(grid, grid_ms)))
+        return grid, grid_ms
+
+    batches = (1, 2, 4, 8, 16, 32, 64)
+    curves = {n: cost_curve(n) for n in batches}
     # greedy continuations (the drafts' reference) from all-AR mixed steps
     prefill(nmax)
     while min(len(sess.state(i)[0]) for i in range(nmax)) < args.prompt + n_ref:
@@ -431,18 +443,18 @@ def concurrency_sweep(args):
                 "n_selfspec": n_ss, "rows": [rows1, rows2], "match_ar": f"{ok}/{n}",
                 "mfma_frac": round(fl / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
-    for n in (1, 2, 4, 8, 16, 32, 64):
+    for n in batches:
         exp = [a_star[i] + 1.0 for i in range(n)]
+        grid, grid_ms = curves[n]
         chosen = tm.choose_modes(grid, grid_ms, exp, k).tolist()
         res = {"metric": "mixed-step committed tokens/s, 8B-class, block 32", "batch": n,
                "expected_tokens_per_round": exp if n <= 8 else f"a*+1 cycling {[a + 1 for a in a_cycle]}",
                "all_ar": run(n, [tm.TRI_AR] * n), "all_selfspec": run(n, [tm.TRI_SELFSPEC] * n),
-               "chosen": run(n, chosen)}
+               "chosen": run(n, chosen),
+               "cost_curve": {"rows": grid, "ms": [round(x, 3) for x in grid_ms]}}
         print(json.dumps(res), flush=True)
     for i in range(nmax):
         sess.set_draft_override(i, None, -1)
-    print(json.dumps({"metric": "forward cost curve, 8B-class decode rows", "rows": grid,
-                      "ms": [round(t, 3) for t in grid_ms]}), flush=True)
 
 
 def sol_analysis(args):

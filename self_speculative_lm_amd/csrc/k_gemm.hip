@@ -224,6 +224,7 @@ __global__ __launch_bounds__(WAVES_PER_WG * 64) void gemm_bf16_kernel(GemmArgs a
 // splits per group.
 struct BigGrid {
   int ntm, nyg, cs;
+  int fpw;  // feature fragments per wave (packed 128-feature blocks per workgroup = fpw)
 };
 
 // Large-M GEMM (prefill chunks and wide batches): the skinny kernel's
@@ -509,21 +510,27 @@ hipError_t launch_pack(int dtype, const WSeg* segs, int nseg, int N, int K, cons
 }
 
 // Which kernel a bf16 GEMM of M rows runs on.  The decode kernel streams W
-// once per 64-row tile; the large-M kernel once per 64-row tile too, but its
-// waves hold four fragments, so each W and X fragment feeds several MFMAs.  Measured on MI355X (8B shapes): the large-M kernel is
-// faster from 65 rows for the wide (N >= 16K) and long-K (K >= 8K) shapes and
-// from 256 rows for the others.
-bool gemm_use_big(int M, int N, int K) { return M > 64 && (M >= 256 || N >= 16384 || K >= 8192); }
+// once per 64-row tile; the large-M kernel once per 64-row tile too (once for
+// all rows in its 128-row form), but its waves hold several fragments, so
+// each W and X fragment feeds several MFMAs.  Measured on MI355X (8B shapes):
+// the large-M kernel is faster from 65 rows for the wide (N >= 16K) and
+// long-K (K >= 8K) shapes and from 192 rows for the others (decode forwards
+// of 224 / 255 rows 9.55 / 9.85 -> 9.29 / 9.56 ms; at 129 rows QKV and o_proj
+// on it were slower).
+bool gemm_use_big(int M, int N, int K) { return M > 64 && (M >= 192 || N >= 16384 || K >= 8192); }
 
-// Large-M form: 8 waves x 2 fragments (256 features) x 4 row tiles (64 rows),
-// 4 k-steps in flight.  Two fragments per wave keep a wave under 128 VGPRs,
-// so two workgroups share a CU (their 64 KB X tiles fit its LDS); with four
-// fragments (512 features, ~180 VGPRs) one workgroup ran per CU.  Measured
-// on MI355X: the 511-row prefill chunk 12.9 -> 11.9 ms, the 8B-class
-// diffusion forward at 16 sequences (512 rows) 16.5 -> 16.1 ms; four row
-// tiles of 128 rows or two of 32 were slower.
-constexpr int BIGM_MT = 4, BIGM_D = 4, BIGM_FPW = 2, BIGM_WAVES = 8;
-constexpr int BIGM_BPW = BIGM_WAVES * BIGM_FPW / 8;  // packed blocks per workgroup
+// Large-M form: 8 waves x 2 or 4 fragments (256 or 512 features) x 4 row
+// tiles (64 rows), 4 k-steps in flight.  With two fragments a wave stays
+// under 128 VGPRs, so two workgroups share a CU (their 64 KB X tiles fit its
+// LDS); with four (~180 VGPRs) one workgroup runs per CU but stages each X
+// tile for twice the features.  The chained form (one slot for all K splits)
+// keeps a running total per fragment, which takes the two-fragment wave to
+// 146 VGPRs: one workgroup per CU either way, so there four fragments win.
+// big_grid picks per launch.  Measured on MI355X: the 511-row prefill chunk
+// 12.9 -> 11.9 ms with two fragments; 8B-class decode forwards of 256 rows
+// 10.25 -> 9.42 ms with four.  Four row tiles of 128 rows or two of 32 were
+// slower.
+constexpr int BIGM_MT = 4, BIGM_D = 4, BIGM_WAVES = 8;
 // Tall form for 65..128 rows: one 128-row tile (8 row tiles) x 1 fragment
 // per wave, so W is streamed once for all the rows instead of once per
 // 64-row tile.  Its per-split partials have the same bits as the other
@@ -536,7 +543,6 @@ constexpr int BIGM_BPW = BIGM_WAVES * BIGM_FPW / 8;  // packed blocks per workgr
 // MI355X, 8B-class diffusion at 4 sequences (128-row forwards): 7.54 ->
 // 6.89 ms per forward.
 constexpr int TALL_MT = 8, TALL_FPW = 1;
-constexpr int TALL_BPW = BIGM_WAVES * TALL_FPW / 8;
 __host__ __forceinline__ bool big_tall(int M) { return M <= TALL_MT * 16; }
 
 // Large-M grid: as few K-split groups (output slots) as keep >= 192
@@ -547,9 +553,10 @@ __host__ __forceinline__ bool big_tall(int M) { return M <= TALL_MT * 16; }
 // order, so either one slot per split, or one slot for all splits with the
 // partials chained in split order (CHAIN); groups of some splits would add
 // in a different order.
-static BigGrid big_grid(const GemmPlan& p, int M, int N, bool invariant) {
+static BigGrid big_grid_for(const GemmPlan& p, int M, int N, bool invariant, int fpw) {
   BigGrid g;
-  const int rows = big_tall(M) ? TALL_MT * 16 : BIGM_MT * 16, bpw = big_tall(M) ? TALL_BPW : BIGM_BPW;
+  const int rows = big_tall(M) ? TALL_MT * 16 : BIGM_MT * 16, bpw = BIGM_WAVES * fpw / 8;
+  g.fpw = fpw;
   g.ntm = (M + rows - 1) / rows;
   const int nfg8 = (((N + GROUP - 1) / GROUP + bpw - 1) / bpw + 7) / 8 * 8;
   g.nyg = p.S;
@@ -561,6 +568,36 @@ static BigGrid big_grid(const GemmPlan& p, int M, int N, bool invariant) {
   if (invariant && g.nyg != 1) g.nyg = p.S;
   g.cs = p.S / g.nyg;
   return g;
+}
+
+// Fragments per wave of a large-M launch.  One for the 128-row form.  Two
+// where the split count is free (prefill chunks): two workgroups per CU and
+// the fewest slots.  Under `invariant`: the fewer output slots first (two
+// fragments can chain all K splits into one slot where four cannot; the
+// consumer kernels then read one slot instead of one per split), then the
+// lighter load on the busiest CU, in two-fragment workgroups' worth of work:
+// a four-fragment workgroup counts 2, a two-fragment one 1, and a chained
+// two-fragment one 1.25 (its running totals take a wave to 146 VGPRs, so it
+// runs alone on its CU with half the waves in flight of two unchained ones).
+// Ties take four fragments, which stage each X tile for twice the features.
+// Fitted to 8B-class decode forwards of 256 to 2112 rows on MI355X (the
+// factor 1.25 is the one value between 1.2 and 1.33 that orders all of them).
+static double big_load(const BigGrid& g, int nfb) {
+  const int bpw = BIGM_WAVES * g.fpw / 8;
+  const long n = (long)((nfb + bpw - 1) / bpw + 7) / 8 * 8 * g.ntm * g.nyg;
+  const double per_cu = (double)((n + 255) / 256);
+  if (g.fpw == 4) return 2.0 * per_cu;
+  return g.cs > 1 ? 1.25 * per_cu : per_cu;
+}
+
+static BigGrid big_grid(const GemmPlan& p, int M, int N, bool invariant) {
+  if (big_tall(M)) return big_grid_for(p, M, N, invariant, TALL_FPW);
+  const BigGrid g2 = big_grid_for(p, M, N, invariant, 2);
+  if (!invariant) return g2;
+  const BigGrid g4 = big_grid_for(p, M, N, invariant, 4);
+  if (g2.nyg != g4.nyg) return g2.nyg < g4.nyg ? g2 : g4;
+  const int nfb = (N + GROUP - 1) / GROUP;
+  return big_load(g2, nfb) < big_load(g4, nfb) ? g2 : g4;
 }
 
 template <int MT, int NCH, int FPW>
@@ -583,8 +620,10 @@ template <int NCH>
 void launch_wide(const GemmArgs& a, const BigGrid& g, bool chain, bool swiglu, bool tall, hipStream_t st) {
   if (tall)
     launch_wide_form<TALL_MT, NCH, TALL_FPW>(a, g, chain, swiglu, st);
+  else if (g.fpw == 4)
+    launch_wide_form<BIGM_MT, NCH, 4>(a, g, chain, swiglu, st);
   else
-    launch_wide_form<BIGM_MT, NCH, BIGM_FPW>(a, g, chain, swiglu, st);
+    launch_wide_form<BIGM_MT, NCH, 2>(a, g, chain, swiglu, st);
 }
 
 // Passes of the large-M kernel as long as possible: the largest NCH <= 8
@@ -603,8 +642,9 @@ int gemm_out_slots(int dtype, const GemmPlan& p, int M, int N, int K, bool invar
 }
 
 bool gemm_swiglu_fused(int dtype, const GemmPlan& p, int M, int N, int K, bool invariant) {
-  return dtype == TRI_BF16 && gemm_use_big(M, N, K) && (big_tall(M) ? TALL_FPW : BIGM_FPW) % 2 == 0 &&
-         big_grid(p, M, N, invariant).nyg == 1;
+  if (dtype != TRI_BF16 || !gemm_use_big(M, N, K)) return false;
+  const BigGrid g = big_grid(p, M, N, invariant);
+  return g.fpw % 2 == 0 && g.nyg == 1;
 }
 
 hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, int N, const GemmPlan& plan, float* P,
@@ -627,7 +667,7 @@ hipError_t launch_gemm(int dtype, const void* X, int M, int K, const void* W, in
       a.nfb = (N + GROUP - 1) / GROUP;
       const BigGrid g = big_grid(plan, M, N, invariant);
       const bool tall = big_tall(M);
-      const int bpw = tall ? TALL_BPW : BIGM_BPW;
+      const int bpw = BIGM_WAVES * g.fpw / 8;
       a.ntiles = ((a.nfb + bpw - 1) / bpw + 7) / 8 * 8 * g.ntm * g.nyg;
       const int nch = wide_nch(plan);
       const bool chain = invariant && g.cs > 1, sw = swiglu_out != nullptr;
@@ -673,8 +713,7 @@ size_t gemm_w_reach(int dtype, const GemmPlan& plan, int M, int N, int K, bool i
   size_t reach = 0;
   if (gemm_use_big(M, N, K)) {
     const BigGrid bg = big_grid(plan, M, N, invariant);
-    const bool tall = big_tall(M);
-    const int FPW = tall ? TALL_FPW : BIGM_FPW, BPW = tall ? TALL_BPW : BIGM_BPW;
+    const int FPW = bg.fpw, BPW = BIGM_WAVES * FPW / 8;
     const int nch = wide_nch(plan), NS = nch * KSTEPS, npass_split = plan.Ks / (nch * KC);
     const long ntiles = (long)((nfb + BPW - 1) / BPW + 7) / 8 * 8 * bg.ntm * bg.nyg;
     for (long id = 0; id < ntiles; ++id) {

@@ -257,6 +257,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGr
   constexpr int XPIECES = MT * 16 * (KC / 8);    // 16-byte pieces of one X stage
   constexpr int XPT = XPIECES / NT;
   static_assert(XPIECES % NT == 0 && (WAVES * FPW) % 8 == 0 && 8 % FPW == 0, "shape");
+  // Prefetch of LDS B fragments one k-step ahead: for the 128-row form only,
+  // whose waves run two per SIMD anyway (the 64-row forms would lose their
+  // second workgroup per CU: 118 -> 130 VGPRs).
+  constexpr bool BPREF = MT >= 8;
   __shared__ bf16x8 xs[2][KSTEPS][MT][64];
   const int id = blockIdx.x;
   const int q = id >> 3, per = bg.ntm * bg.nyg;
@@ -326,12 +330,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGr
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (c + 1 < NCH) load_x(c + 1);
+      // BPREF: the B fragments of the stage's next k-step are read from LDS
+      // before the MFMAs of this one, so their latency hides behind them.
+      bf16x8 bcur[MT];
+      if constexpr (BPREF) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) bcur[t] = xs[c & 1][0][t][lane];
+      }
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const int j = c * KSTEPS + s;
+        bf16x8 bnext[MT];
+        if constexpr (BPREF) {
+          if (s + 1 < KSTEPS) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) bnext[t] = xs[c & 1][s + 1][t][lane];
+          }
+        }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const bf16x8 bv = xs[c & 1][s][t][lane];
+          const bf16x8 bv = BPREF ? bcur[t] : xs[c & 1][s][t][lane];
 #pragma unroll
           for (int f = 0; f < FPW; ++f)
             acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[j % D][f], bv, acc[f][t], 0, 0, 0);
@@ -341,6 +359,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_wide_kernel(GemmArgs a, BigGr
           for (int f = 0; f < FPW; ++f) ring[j % D][f] = ld16(wp + (size_t)(j + D) * wstep + f * 512);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (BPREF) {
+          if (s + 1 < KSTEPS) {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) bcur[t] = bnext[t];
+          }
+        }
       }
       if (c + 1 < NCH) {
         store_x((c + 1) & 1);

@@ -820,7 +820,11 @@ def main():
                      "kernel": "gemm_bf16_kernel (gate/up projection, N=24576, K=4096)",
                      "avg_launch_us": round(gu_avg_ms * 1e3, 2), "launches": gu_n,
                      "frac_of_device_copy": round(gu_gbs / copy_gbs, 4) if copy_gbs == copy_gbs else None,
-                     "algorithmic_bytes_per_launch": int(gu_bytes)},
+                     "algorithmic_bytes_per_launch": int(gu_bytes),
+                     # the whole round (both forwards, every kernel) against the same peak
+                     "step": {"achieved": round(round_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(round_gbs / HBM_PEAK_GBS, 4),
+                              "algorithmic_bytes_per_round": int(fwd_bytes)}},
     }
 
     if not args.no_replay:

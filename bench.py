@@ -109,6 +109,27 @@ def cpu_baseline(shape, prefix, k, tpr, repeats=5):
     per_layer = times[2] - times[1]
     head = times[1] - per_layer
     round_s = head + shape.n_layers * per_layer
+    # The tiny float32 configuration (2 layers, d 128, 16-token prompt) run in
+    # full on one BLAS thread: 32 new tokens in each of AR, diffusion (block 8,
+    # threshold 0.9) and self-speculation (block 8).
+    tiny = None
+    try:
+        from threadpoolctl import threadpool_limits
+        from oracle import OracleSession
+        from oracle.decode import MODE_AR, MODE_DIFFUSION, MODE_SELFSPEC
+        tshape, n_new, tb = seeded.TINY, 32, 8
+        tom = OracleModel(tshape, seeded.gen_weights(tshape))
+        tprompt = seeded.prompt(16, tshape.vocab)
+        tiny = {"unit": "tok/s", "threads": 1, "new_tokens": n_new, "block": tb, "threshold": 0.9}
+        with threadpool_limits(limits=1):
+            for name, mode in (("ar", MODE_AR), ("diffusion", MODE_DIFFUSION), ("selfspec", MODE_SELFSPEC)):
+                ts_ = OracleSession(tom, 16 + n_new + 2 * tb + 8)
+                ts_.prefill(tprompt)
+                t0 = time.perf_counter()
+                ts_.generate(mode, n_new, tb, 0.9)
+                tiny[name] = round(n_new / (time.perf_counter() - t0), 1)
+    except ImportError:  # the figure is context only
+        tiny = None
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -116,7 +137,8 @@ def cpu_baseline(shape, prefix, k, tpr, repeats=5):
     except OSError:
         pass
     return {"value": round(tpr / round_s, 4), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
-            "cpu_model": cpu_model, "host_cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model, "host_cpu_count": os.cpu_count(), "blas_threads": int(threads),
+            "tiny_1thread": tiny,
             "sample": (f"float64 oracle (float32-stored weights, batched row products), one draft ({k + 1} rows) + "
                        f"one verify ({k} rows) forward over 1- and 2-layer slices of the 8B-class model with a "
                        f"{prefix}-token cache, {repeats} times each; mean per-layer time {per_layer:.3f}s, "

@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "tri_common.h"
 
@@ -27,16 +28,22 @@ __device__ __forceinline__ float slot_sum(const float* P, int nslots, size_t str
   return acc;
 }
 
-// The same for four consecutive columns (off % 4 == 0, stride % 4 == 0).
-__device__ __forceinline__ f32x4 slot_sum4(const float* P, int nslots, size_t stride, size_t off) {
-  f32x4 v[MAX_SLOTS];
+// Four consecutive columns (off % 4 == 0, stride % 4 == 0) with the slot
+// count known at compile time: every load is issued
+// unconditionally before the first add, so the sum costs one memory round
+// trip.  (A runtime count compiles to one branch per slot, and the join
+// after each branch made the compiler wait for the loads already issued:
+// two round trips instead of one.)  Same additions in the same order as
+// slot_sum.
+template <int NS>
+__device__ __forceinline__ f32x4 slot_sum4n(const float* P, size_t stride, size_t off) {
+  static_assert(NS >= 1 && NS <= MAX_SLOTS, "slot count");
+  f32x4 v[NS];
 #pragma unroll
-  for (int s = 0; s < MAX_SLOTS; ++s)
-    v[s] = s < nslots ? *reinterpret_cast<const f32x4*>(P + s * stride + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < NS; ++s) v[s] = *reinterpret_cast<const f32x4*>(P + s * stride + off);
   f32x4 acc = v[0];
 #pragma unroll
-  for (int s = 1; s < MAX_SLOTS; ++s)
-    if (s < nslots) acc += v[s];
+  for (int s = 1; s < NS; ++s) acc += v[s];
   return acc;
 }
 
@@ -65,39 +72,35 @@ __global__ __launch_bounds__(1024) void embed_kernel(const int32_t* tok, const T
 }
 
 // x[r] += sum of slots; y[r] = x[r] / sqrt(mean(x[r]^2) + eps) * g   (RMSNorm).
-// One 1024-thread workgroup per row, four columns per thread per pass.  The
-// mean square is taken in a fixed order (16-column chunks, then one wave over
-// the chunks: sumsq4 / row_total).
-constexpr int NORM_THREADS = 1024;
-constexpr int NORM_VPT = 2;  // float4 groups per thread: d <= 1024 * 4 * 2
-// gamma is read with the row, before the reduction, and y is written with
-// one vector store per four columns.
-template <typename T>
-__global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* __restrict__ x,
-                                                                  const float* __restrict__ P, int nslots,
-                                                                  size_t stride, int d,
-                                                                  const float* __restrict__ g, float eps,
-                                                                  T* __restrict__ y) {
-  __shared__ float chunk[NORM_THREADS * NORM_VPT / 4];
+// One workgroup per row, VPT groups of four columns per thread (the
+// launcher sizes the workgroup so that every group lies in the row, except
+// for the last workgroup rounding).  Every load of the row (x, g, the NS
+// slots of each group) is issued before the first use, at a clamped address
+// for a group past the row, and x is written back with y at the end, so the
+// kernel makes one memory round trip.  The mean square is taken in a fixed
+// order (16-column chunks, then one wave over the chunks: sumsq4 / row_total).
+constexpr int NORM_CHUNKS = 512;  // 16-column chunks: d <= 8192
+template <typename T, int NS, int VPT>
+__global__ __launch_bounds__(VPT == 1 ? 1024 : (VPT == 2 ? 640 : 512)) void resid_norm_kernel(
+    float* __restrict__ x, const float* __restrict__ P, size_t stride, int d, const float* __restrict__ g,
+    float eps, T* __restrict__ y) {
+  __shared__ float chunk[NORM_CHUNKS];
   __shared__ float tot_s;
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   float* xr = x + (size_t)r * d;
-  f32x4 v[NORM_VPT], gv[NORM_VPT];
+  f32x4 v[VPT], gv[VPT];
 #pragma unroll
-  for (int i = 0; i < NORM_VPT; ++i) {
-    const int c = (tid + i * NORM_THREADS) * 4;
-    f32x4 val = {0.f, 0.f, 0.f, 0.f};
-    gv[i] = val;
-    if (c < d) {
-      gv[i] = *reinterpret_cast<const f32x4*>(g + c);
-      val = *reinterpret_cast<const f32x4*>(xr + c);
-      if (nslots > 0) {
-        val += slot_sum4(P, nslots, stride, (size_t)r * d + c);
-        *reinterpret_cast<f32x4*>(xr + c) = val;
-      }
-    }
-    v[i] = val;
-    float q = sumsq4(val);
+  for (int i = 0; i < VPT; ++i) {
+    const int c = min((tid + i * nt) * 4, d - 4);
+    gv[i] = *reinterpret_cast<const f32x4*>(g + c);
+    v[i] = *reinterpret_cast<const f32x4*>(xr + c);
+    if constexpr (NS > 0) v[i] += slot_sum4n<NS>(P, stride, (size_t)r * d + c);
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = (tid + i * nt) * 4;
+    if (c >= d) v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float q = sumsq4(v[i]);
     q += __shfl_xor(q, 1);
     q += __shfl_xor(q, 2);
     if ((tid & 3) == 0 && c < d) chunk[c / 16] = q;
@@ -110,9 +113,12 @@ __global__ __launch_bounds__(NORM_THREADS) void resid_norm_kernel(float* __restr
   __syncthreads();
   const float inv = rms_inv(tot_s, d, eps);
 #pragma unroll
-  for (int i = 0; i < NORM_VPT; ++i) {
-    const int c = (tid + i * NORM_THREADS) * 4;
-    if (c < d) Elem<T>::store4(y, (size_t)r * d + c, v[i] * inv * gv[i]);
+  for (int i = 0; i < VPT; ++i) {
+    const int c = (tid + i * nt) * 4;
+    if (c < d) {
+      Elem<T>::store4(y, (size_t)r * d + c, v[i] * inv * gv[i]);
+      if constexpr (NS > 0) *reinterpret_cast<f32x4*>(xr + c) = v[i];
+    }
   }
 }
 
@@ -185,8 +191,8 @@ __global__ __launch_bounds__(64 * ROPE_HEADS) void rope_kv_kernel(const float* _
 // form) to the row scratch as rope_kv_kernel does.
 constexpr int ROPE128_HPW = 4;                    // heads per wave
 constexpr int ROPE128_HEADS = 4 * ROPE128_HPW;    // heads per 256-thread workgroup
-template <typename T, bool VF16 = false>
-__global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict__ P, int nslots, size_t stride,
+template <typename T, bool VF16, int NS>
+__global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict__ P, size_t stride,
                                                          int hq, int hkv, const int32_t* row_seq,
                                                          const int32_t* row_pos, const float* __restrict__ rope,
                                                          T* __restrict__ qout, T* __restrict__ kc,
@@ -198,10 +204,10 @@ __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict
   if (h >= hq + 2 * hkv) return;
   const int c = 4 * (threadIdx.x & 15);
   const int pos = row_pos[r], seq = row_seq[r];
-  const bool scr = bs.blk && bs.blk[r] >= 0;
   const size_t rb = (size_t)r * (hq + 2 * hkv) * hd + (size_t)h * hd;
-  const f32x4 xa = slot_sum4(P, nslots, stride, rb + c);
-  const f32x4 xb = slot_sum4(P, nslots, stride, rb + c + half);
+  const f32x4 xa = slot_sum4n<NS>(P, stride, rb + c);
+  const f32x4 xb = slot_sum4n<NS>(P, stride, rb + c + half);
+  const bool scr = bs.blk && bs.blk[r] >= 0;
   if (h < hq + hkv) {
     const f32x4 t0 = *reinterpret_cast<const f32x4*>(rope + ((size_t)pos * half + c) * 2);
     const f32x4 t1 = *reinterpret_cast<const f32x4*>(rope + ((size_t)pos * half + c) * 2 + 4);
@@ -252,16 +258,16 @@ __global__ __launch_bounds__(256) void rope_kv128_kernel(const float* __restrict
 // of 16 (the weight packing's order): columns [32j, 32j+16) are gate
 // features [16j, 16j+16) and [32j+16, 32j+32) the matching up features.
 // One thread per four consecutive columns of h in one row.
-template <typename T>
-__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ P, int nslots, size_t stride,
-                                                     int rows, int ffn, T* __restrict__ h) {
+template <typename T, int NS>
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ P, size_t stride, int rows, int ffn,
+                                                     T* __restrict__ h) {
   const int q4 = ffn / 4;
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * q4) return;
   const int r = i / q4, c = (i - r * q4) * 4;
   const size_t rb = (size_t)r * 2 * ffn + (size_t)(c >> 4) * 32 + (c & 15);
-  const f32x4 gt = slot_sum4(P, nslots, stride, rb);
-  const f32x4 up = slot_sum4(P, nslots, stride, rb + 16);
+  const f32x4 gt = slot_sum4n<NS>(P, stride, rb);
+  const f32x4 up = slot_sum4n<NS>(P, stride, rb + 16);
   f32x4 o;
 #pragma unroll
   for (int e = 0; e < 4; ++e) o[e] = gt[e] / (1.0f + expf(-gt[e])) * up[e];
@@ -493,16 +499,43 @@ hipError_t launch_embed(int dtype, const int32_t* tok, int rows, const void* E, 
   return hipGetLastError();
 }
 
+// Calls fn(std::integral_constant<int, n>) for a slot count n in [K, MAX_SLOTS].
+template <int K, typename Fn>
+hipError_t with_slots(int n, Fn& fn) {
+  if constexpr (K > MAX_SLOTS) {
+    return hipErrorInvalidValue;
+  } else {
+    return n == K ? fn(std::integral_constant<int, K>{}) : with_slots<K + 1>(n, fn);
+  }
+}
+
+// Four columns per thread in one pass up to 4096 columns (1024 threads), two
+// passes up to 5120 (640 threads), four up to 8192 (512 threads).
 hipError_t launch_resid_norm(int dtype, float* x, const float* P, int nslots, size_t stride, int rows,
                              int d, const float* g, float eps, void* y, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (d > NORM_THREADS * 4 * NORM_VPT || d % 16 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
-  TRI_DISPATCH(dtype,
-               hipLaunchKernelGGL(resid_norm_kernel<float>, dim3(rows), dim3(NORM_THREADS), 0, st, x, P, nslots,
-                                  stride, d, g, eps, static_cast<float*>(y)),
-               hipLaunchKernelGGL(resid_norm_kernel<bf16_t>, dim3(rows), dim3(NORM_THREADS), 0, st, x, P,
-                                  nslots, stride, d, g, eps, static_cast<bf16_t*>(y)));
-  return hipGetLastError();
+  if (d > NORM_CHUNKS * 16 || d % 16 || nslots < 0 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  const int vpt = d <= 4096 ? 1 : (d <= 5120 ? 2 : 4);
+  const int threads = ((d / 4 + vpt - 1) / vpt + 63) / 64 * 64;
+  auto launch = [&](auto ns) -> hipError_t {
+    constexpr int NS = decltype(ns)::value;
+    auto go = [&](auto vp) {
+      constexpr int V = decltype(vp)::value;
+      TRI_DISPATCH(dtype,
+                   hipLaunchKernelGGL((resid_norm_kernel<float, NS, V>), dim3(rows), dim3(threads), 0, st, x, P,
+                                      stride, d, g, eps, static_cast<float*>(y)),
+                   hipLaunchKernelGGL((resid_norm_kernel<bf16_t, NS, V>), dim3(rows), dim3(threads), 0, st, x, P,
+                                      stride, d, g, eps, static_cast<bf16_t*>(y)));
+    };
+    if (vpt == 1)
+      go(std::integral_constant<int, 1>{});
+    else if (vpt == 2)
+      go(std::integral_constant<int, 2>{});
+    else
+      go(std::integral_constant<int, 4>{});
+    return hipGetLastError();
+  };
+  return with_slots<0>(nslots, launch);
 }
 
 hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, int rows, int hq, int hkv,
@@ -510,25 +543,28 @@ hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, 
                           void* qout, void* kc, void* vc, int ctx, size_t css, hipStream_t st, bool v_f16,
                           int32_t* vsat, const int32_t* row_blk, void* kscr, void* vscr) {
   if (rows <= 0) return hipSuccess;
-  if (nslots > MAX_SLOTS || (v_f16 && (dtype != TRI_BF16 || hd != 128))) return hipErrorInvalidValue;
+  if (nslots < 1 || nslots > MAX_SLOTS || (v_f16 && (dtype != TRI_BF16 || hd != 128))) return hipErrorInvalidValue;
   if (row_blk && (!kscr || !vscr)) return hipErrorInvalidValue;
   const BlockScratch bs{row_blk, kscr, vscr};
   if (hd == 128) {
     const dim3 grid128(rows, (hq + 2 * hkv + ROPE128_HEADS - 1) / ROPE128_HEADS);
-    if (v_f16) {
-      hipLaunchKernelGGL((rope_kv128_kernel<bf16_t, true>), grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
-                         row_seq, row_pos, rope, static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
-                         static_cast<bf16_t*>(vc), ctx, css, vsat, bs);
+    auto launch = [&](auto ns) -> hipError_t {
+      constexpr int NS = decltype(ns)::value;
+      if (v_f16)
+        hipLaunchKernelGGL((rope_kv128_kernel<bf16_t, true, NS>), grid128, dim3(256), 0, st, P, stride, hq, hkv,
+                           row_seq, row_pos, rope, static_cast<bf16_t*>(qout), static_cast<bf16_t*>(kc),
+                           static_cast<bf16_t*>(vc), ctx, css, vsat, bs);
+      else
+        TRI_DISPATCH(dtype,
+                     hipLaunchKernelGGL((rope_kv128_kernel<float, false, NS>), grid128, dim3(256), 0, st, P, stride,
+                                        hq, hkv, row_seq, row_pos, rope, static_cast<float*>(qout),
+                                        static_cast<float*>(kc), static_cast<float*>(vc), ctx, css, vsat, bs),
+                     hipLaunchKernelGGL((rope_kv128_kernel<bf16_t, false, NS>), grid128, dim3(256), 0, st, P,
+                                        stride, hq, hkv, row_seq, row_pos, rope, static_cast<bf16_t*>(qout),
+                                        static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, css, vsat, bs));
       return hipGetLastError();
-    }
-    TRI_DISPATCH(dtype,
-                 hipLaunchKernelGGL(rope_kv128_kernel<float>, grid128, dim3(256), 0, st, P, nslots, stride, hq, hkv,
-                                    row_seq, row_pos, rope, static_cast<float*>(qout), static_cast<float*>(kc),
-                                    static_cast<float*>(vc), ctx, css, vsat, bs),
-                 hipLaunchKernelGGL(rope_kv128_kernel<bf16_t>, grid128, dim3(256), 0, st, P, nslots, stride, hq,
-                                    hkv, row_seq, row_pos, rope, static_cast<bf16_t*>(qout),
-                                    static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), ctx, css, vsat, bs));
-    return hipGetLastError();
+    };
+    return with_slots<1>(nslots, launch);
   }
   const dim3 grid(rows, (hq + 2 * hkv + ROPE_HEADS - 1) / ROPE_HEADS);
   TRI_DISPATCH(dtype,
@@ -545,14 +581,18 @@ hipError_t launch_rope_kv(int dtype, const float* P, int nslots, size_t stride, 
 hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t stride, int rows, int ffn, void* h,
                          hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (ffn % 16 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  if (ffn % 16 || nslots < 1 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(((size_t)rows * (ffn / 4) + 255) / 256));
-  TRI_DISPATCH(dtype,
-               hipLaunchKernelGGL(swiglu_kernel<float>, grid, dim3(256), 0, st, P, nslots, stride, rows,
-                                  ffn, static_cast<float*>(h)),
-               hipLaunchKernelGGL(swiglu_kernel<bf16_t>, grid, dim3(256), 0, st, P, nslots, stride, rows,
-                                  ffn, static_cast<bf16_t*>(h)));
-  return hipGetLastError();
+  auto launch = [&](auto ns) -> hipError_t {
+    constexpr int NS = decltype(ns)::value;
+    TRI_DISPATCH(dtype,
+                 hipLaunchKernelGGL((swiglu_kernel<float, NS>), grid, dim3(256), 0, st, P, stride, rows, ffn,
+                                    static_cast<float*>(h)),
+                 hipLaunchKernelGGL((swiglu_kernel<bf16_t, NS>), grid, dim3(256), 0, st, P, stride, rows, ffn,
+                                    static_cast<bf16_t*>(h)));
+    return hipGetLastError();
+  };
+  return with_slots<1>(nslots, launch);
 }
 
 hipError_t launch_lora_mid(int dtype, const float* P, int nslots, size_t stride, int rows, int rk,

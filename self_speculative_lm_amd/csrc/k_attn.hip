@@ -434,11 +434,12 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
 // split gets the same bits whether or not other rows of the launch need
 // more splits.
 // One workgroup per (row, 4 heads), one thread per output element.
-template <typename T>
+// B: partials loaded per batch, the launch's split count rounded up to 4, 8
+// or 16 (the merge order, and so the result, does not depend on it).
+template <typename T, int B>
 __global__ __launch_bounds__(512) void attn_combine_kernel(const float* part_o, const float* part_ml,
                                                            const int32_t* row_hi, int rows, int hq, int hd,
                                                            int kv_split, int nsplit, T* out) {
-  constexpr int B = 16;
   const int row = blockIdx.x, head = blockIdx.y * 4 + (int)threadIdx.x / HD, d = threadIdx.x % HD;
   if (head >= hq) return;
   const int hi = row_hi[row];
@@ -794,8 +795,16 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
     return hipGetLastError();
   }
   if (a.nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(L.rows, (L.hq + 3) / 4), dim3(4 * HD), 0, st, a.part_o, a.part_ml,
-                     L.row_hi, L.rows, L.hq, HD, L.kv_split, a.nsplit, a.out);
+  const dim3 cgrid(L.rows, (L.hq + 3) / 4), cblock(4 * HD);
+  if (a.nsplit <= 4)
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 4>), cgrid, cblock, 0, st, a.part_o, a.part_ml, L.row_hi,
+                       L.rows, L.hq, HD, L.kv_split, a.nsplit, a.out);
+  else if (a.nsplit <= 8)
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 8>), cgrid, cblock, 0, st, a.part_o, a.part_ml, L.row_hi,
+                       L.rows, L.hq, HD, L.kv_split, a.nsplit, a.out);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 16>), cgrid, cblock, 0, st, a.part_o, a.part_ml, L.row_hi,
+                       L.rows, L.hq, HD, L.kv_split, a.nsplit, a.out);
   return hipGetLastError();
 }
 

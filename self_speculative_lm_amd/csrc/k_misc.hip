@@ -274,14 +274,22 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ P
   Elem<T>::store4(h, (size_t)r * ffn + c, o);
 }
 
-// LoRA middle activation A o, kept only on flagged rows (zero elsewhere).
-template <typename T>
-__global__ void lora_mid_kernel(const float* P, int nslots, size_t stride, int rk,
-                                const int32_t* row_lora, T* mid) {
+// LoRA middle activation A o, kept only on flagged rows (zero elsewhere);
+// NS slots, all loaded before the first add (slot_sum's order).
+template <typename T, int NS>
+__global__ void lora_mid_kernel(const float* P, size_t stride, int rk, const int32_t* row_lora, T* mid) {
   const int r = blockIdx.x;
   const bool on = row_lora[r] != 0;
-  for (int c = threadIdx.x; c < rk; c += blockDim.x)
-    Elem<T>::store(mid, (size_t)r * rk + c, on ? slot_sum(P, nslots, stride, (size_t)r * rk + c) : 0.f);
+  for (int c = threadIdx.x; c < rk; c += blockDim.x) {
+    const size_t off = (size_t)r * rk + c;
+    float v[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) v[s] = P[s * stride + off];
+    float acc = v[0];
+#pragma unroll
+    for (int s = 1; s < NS; ++s) acc += v[s];
+    Elem<T>::store(mid, off, on ? acc : 0.f);
+  }
 }
 
 __global__ void zero_kernel(float* p, size_t n) {
@@ -598,12 +606,17 @@ hipError_t launch_swiglu(int dtype, const float* P, int nslots, size_t stride, i
 hipError_t launch_lora_mid(int dtype, const float* P, int nslots, size_t stride, int rows, int rk,
                            const int32_t* row_lora, void* mid, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  TRI_DISPATCH(dtype,
-               hipLaunchKernelGGL(lora_mid_kernel<float>, dim3(rows), dim3(128), 0, st, P, nslots, stride,
-                                  rk, row_lora, static_cast<float*>(mid)),
-               hipLaunchKernelGGL(lora_mid_kernel<bf16_t>, dim3(rows), dim3(128), 0, st, P, nslots,
-                                  stride, rk, row_lora, static_cast<bf16_t*>(mid)));
-  return hipGetLastError();
+  if (nslots < 1 || nslots > MAX_SLOTS) return hipErrorInvalidValue;
+  auto launch = [&](auto ns) -> hipError_t {
+    constexpr int NS = decltype(ns)::value;
+    TRI_DISPATCH(dtype,
+                 hipLaunchKernelGGL((lora_mid_kernel<float, NS>), dim3(rows), dim3(128), 0, st, P, stride, rk,
+                                    row_lora, static_cast<float*>(mid)),
+                 hipLaunchKernelGGL((lora_mid_kernel<bf16_t, NS>), dim3(rows), dim3(128), 0, st, P, stride, rk,
+                                    row_lora, static_cast<bf16_t*>(mid)));
+    return hipGetLastError();
+  };
+  return with_slots<1>(nslots, launch);
 }
 
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st) {

@@ -370,8 +370,8 @@ def quadratic_sweep(args):
 
 def concurrency_sweep(args):
     """Mixed AR / self-speculation steps on the 8B-class decoder at 1..64
-    sequences.  First, for each batch n, the cost of one forward over the n
-    sequences at row counts from n to n x (k+1); then for each n the committed
+    sequences.  First, for each batch n, the per-forward cost of its mixed
+    steps with 0..n self-speculation sequences (rows n to n x (k+1)); then for each n the committed
     tokens/s of all-AR steps, all-self-speculation steps and the per-sequence
     choice of tri_choose_modes from that batch's curve.  Acceptance is
     controlled per sequence: its drafts are the GPU's own greedy continuation
@@ -402,34 +402,7 @@ def concurrency_sweep(args):
         torch.cuda.synchronize()
 
     prefill(nmax)
-    # points on both sides of the GEMM form switches (64 | 65 and 128 | 129 rows)
-    # so the interpolated cost sees their steps
-    base_grid = [1, 2, 4, 8, 16, 32, 64, 65, 96, 128, 129, 192, 256, 384, 512, 768, 1024, 1536]
-
-    def cost_curve(n):
-        """Teacher-forced forwards (full lm_head and sampling) of R rows spread
-        over n sequences as causal rows from each pending position, for R from
-        n (all AR) to n (k + 1) (all self-speculation): the attention reads the
-        same n caches whatever the mode mix, so the curve is taken per batch."""
-        grid = sorted({n, n * (k + 1)} | {g for g in base_grid if n < g < n * (k + 1)})
-        grid_ms = []
-        for R in grid:
-            per = [R // n + (1 if i < R % n else 0) for i in range(n)]
-            seq = np.concatenate([np.full(c, i) for i, c in enumerate(per)]).astype(np.int32)
-            pos = np.concatenate([args.prompt - 1 + np.arange(c) for c in per]).astype(np.int32)
-            tok = np.array([prompts[i][j % args.prompt] for i, c in enumerate(per) for j in range(c)], dtype=np.int32)
-            ts = []
-            for rep in range(6):
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                sess.forward(seq, tok, pos, pos + 1)
-                ts.append(time.perf_counter() - t0)
-            grid_ms.append(float(np.median(ts[1:])) * 1e3)
-        log(f"{n} sequences: forward over " + ", ".join(f"{R} rows {m:.2f} ms" for R, m in zip(grid, grid_ms)))
-        return grid, grid_ms
-
     batches = (1, 2, 4, 8, 16, 32, 64)
-    curves = {n: cost_curve(n) for n in batches}
     # greedy continuations (the drafts' reference) from all-AR mixed steps
     prefill(nmax)
     while min(len(sess.state(i)[0]) for i in range(nmax)) < args.prompt + n_ref:
@@ -464,6 +437,26 @@ def concurrency_sweep(args):
         return {"tok_s": round(committed / dt, 1), "ms_per_step": round(dt * 1e3 / steps, 3),
                 "n_selfspec": n_ss, "rows": [rows1, rows2], "match_ar": f"{ok}/{n}",
                 "mfma_frac": round(fl / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    def cost_curve(n):
+        """Per-forward cost of the batch's mixed steps: for s self-speculation
+        sequences among n (s from 0 to n, denser where few), one timed mixed
+        step of n + k s draft and n + (k - 1) s verify rows, half its time
+        charged to each forward and read as the cost at n + k s rows.  The
+        policy then interpolates what it will actually run.  (Teacher-forced
+        forwards of the same rows undercount a mixed step: at 64 sequences
+        one 33-row sequence among 63 single rows took 14.6 ms per step against
+        12.4 ms read from such a curve, which turned a near-tie the wrong way.)"""
+        counts = sorted({s for s in (0, 1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64) if s <= n} | {n})
+        grid, grid_ms = [], []
+        for s in counts:
+            r = run(n, [tm.TRI_SELFSPEC] * s + [tm.TRI_AR] * (n - s))
+            grid.append(n + k * s)
+            grid_ms.append(r["ms_per_step"] / 2)
+        log(f"{n} sequences: forward over " + ", ".join(f"{R} rows {m:.2f} ms" for R, m in zip(grid, grid_ms)))
+        return grid, grid_ms
+
+    curves = {n: cost_curve(n) for n in batches}
 
     for n in batches:
         exp = [a_star[i] + 1.0 for i in range(n)]

@@ -63,6 +63,11 @@ struct AttnArgs {
   float* part_ml;  // [nsplit][rows][hq][2]
   int qgroups, nz;  // query groups per (split, sequence x kv head); n_seq * hkv
   int force_part;   // write partials even with one split (a combine follows)
+  // Compacted grid (NULL: every sequence gets qgroups query groups): entry w
+  // = slot * 65536 + query group, only the groups that hold query vectors;
+  // workgroup id = (w * hkv + kv head) * nsplit + split.
+  const int32_t* work;
+  int nwork;
 };
 
 __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
@@ -114,11 +119,27 @@ __global__ __launch_bounds__(QW * KW * 64) void attn_bf16_kernel(AttnArgs a) {
   // Workgroup id -> (split bx, query group bq, sequence x kv head bz).  The
   // query groups of one (split, kv head) get ids 8 apart, so they run on one
   // XCD one after the other and the later ones find the K/V tiles in its L2.
-  const int per = 8 * a.qgroups;
-  const int pr = ((int)blockIdx.x / per) * 8 + ((int)blockIdx.x & 7);
-  if (pr >= a.nsplit * a.nz) return;
-  const int bq = ((int)blockIdx.x % per) >> 3, bx = pr % a.nsplit, bz = pr / a.nsplit;
-  const int seq = bz / a.hkv, kvh = bz - seq * a.hkv;
+  int bq, bx, seq, kvh;
+  if (a.work) {
+    // compacted grid: the query groups of one (slot, kv head, split) are
+    // hkv * nsplit ids apart (a multiple of 8 for 8 kv heads: one XCD)
+    const int id = (int)blockIdx.x;
+    bx = id % a.nsplit;
+    const int t = id / a.nsplit;
+    kvh = t % a.hkv;
+    const int e = a.work[t / a.hkv];
+    seq = e >> 16;
+    bq = e & 0xffff;
+  } else {
+    const int per = 8 * a.qgroups;
+    const int pr = ((int)blockIdx.x / per) * 8 + ((int)blockIdx.x & 7);
+    if (pr >= a.nsplit * a.nz) return;
+    bq = ((int)blockIdx.x % per) >> 3;
+    bx = pr % a.nsplit;
+    const int bz = pr / a.nsplit;
+    seq = bz / a.hkv;
+    kvh = bz - seq * a.hkv;
+  }
   const int G = a.hq / a.hkv;
   const int cseq = a.slot_seq ? a.slot_seq[seq] : seq;
   const int r0 = a.seq_start[seq];
@@ -723,6 +744,38 @@ int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int 
   return t64 <= 0.9 * t2 ? best64 : best2;
 }
 
+int attn_group_vectors(int max_rows_per_seq, int G, int max_hi) {
+  int qw, qt;
+  attn_shape((max_rows_per_seq * G + 15) / 16, max_hi, &qw, &qt);
+  return qw * 16 * qt;
+}
+
+// Compacted attention grid of a forward (see AttnArgs::work): one entry per
+// (slot, query group) that holds query vectors, under the launch shape
+// launch_attn takes for these rows.  0 when every slot has the same number
+// of groups (the regular grid launches no empty workgroup) or the table
+// would pass `cap` entries.  Measured on MI355X, 64 sequences with one
+// 33-row block among single rows: the regular grid launched 2048-2560
+// workgroups, most of them empty, and the attention took 44-94 us against
+// 36 us for single rows only.
+int attn_work_table(const int32_t* seq_start, int n_slots, int hq, int hkv, int max_hi, int32_t* out, int cap) {
+  if (n_slots < 2 || hkv < 1) return 0;
+  const int G = hq / hkv;
+  int max_rows = 0;
+  for (int i = 0; i < n_slots; ++i) max_rows = std::max(max_rows, seq_start[i + 1] - seq_start[i]);
+  const int qv = attn_group_vectors(max_rows, G, max_hi);
+  int w = 0;
+  bool uniform = true;
+  const int g0 = ((seq_start[1] - seq_start[0]) * G + qv - 1) / qv;
+  for (int i = 0; i < n_slots; ++i) {
+    const int groups = ((seq_start[i + 1] - seq_start[i]) * G + qv - 1) / qv;
+    uniform = uniform && groups == g0;
+    if (groups > 65535 || w + groups > cap) return 0;
+    for (int g = 0; g < groups; ++g) out[w++] = i * 65536 + g;
+  }
+  return uniform ? 0 : w;
+}
+
 size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split) {
   if (kv_split <= 0) kv_split = 128;  // the shortest split any pick makes: an upper bound
   const size_t ns = (size_t)((max_hi + kv_split - 1) / kv_split);
@@ -768,9 +821,12 @@ hipError_t launch_attn(int dtype, const AttnLaunch& L, hipStream_t st) {
   const int qgroups = (qtiles + qw * qt - 1) / (qw * qt);
   a.qgroups = qgroups;
   a.nz = L.n_seq * L.hkv;
+  a.work = L.work;
+  a.nwork = L.nwork;
   const long pairs8 = ((long)a.nsplit * a.nz + 7) / 8 * 8;
   if (pairs8 * qgroups > 0x7fffffffL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(pairs8 * qgroups));
+  if (L.work && (L.nwork < 1 || (long)L.nwork * L.hkv * a.nsplit > 0x7fffffffL)) return hipErrorInvalidValue;
+  const dim3 grid(L.work ? (unsigned)((long)L.nwork * L.hkv * a.nsplit) : (unsigned)(pairs8 * qgroups));
   if (L.v_f16) {
     if (qw == 2)
       hipLaunchKernelGGL((attn_bf16_kernel<2, 2, 1, true>), grid, dim3(256), 0, st, a);

@@ -83,7 +83,8 @@ struct Seq {
 
 // Row metadata of one forward: a host (pinned) mirror and a device copy.
 struct MetaLayout {
-  size_t tok, pos, hi, seq, lora, kind, blk, seq_start, slot_seq, block_start, sidx, didx, size;
+  size_t tok, pos, hi, seq, lora, kind, blk, seq_start, slot_seq, block_start, sidx, didx, awork, size;
+  int awork_cap;
 };
 MetaLayout meta_layout(int max_rows, int max_batch) {
   MetaLayout L;
@@ -105,17 +106,19 @@ MetaLayout meta_layout(int max_rows, int max_batch) {
   L.block_start = take(max_batch + 1);
   L.sidx = take(2 * (size_t)max_rows + 2 * max_batch);
   L.didx = take(2 * (size_t)max_rows + 2 * max_batch);
+  L.awork_cap = max_rows + max_batch;  // (slot, query group) entries: enough up to 32 query heads per kv head
+  L.awork = take((size_t)L.awork_cap);
   L.size = o;
   return L;
 }
 
 struct Meta {
-  int32_t *tok, *pos, *hi, *seq, *lora, *kind, *blk, *seq_start, *slot_seq, *block_start, *sidx, *didx;
+  int32_t *tok, *pos, *hi, *seq, *lora, *kind, *blk, *seq_start, *slot_seq, *block_start, *sidx, *didx, *awork;
 };
 Meta meta_ptrs(int32_t* base, size_t off, const MetaLayout& L) {
   int32_t* b = base + off;
   return Meta{b + L.tok,  b + L.pos,       b + L.hi,          b + L.seq,         b + L.lora, b + L.kind, b + L.blk,
-              b + L.seq_start, b + L.slot_seq, b + L.block_start, b + L.sidx, b + L.didx};
+              b + L.seq_start, b + L.slot_seq, b + L.block_start, b + L.sidx, b + L.didx, b + L.awork};
 }
 
 // The layout of a forward's metadata is sized by its own rows (rounded up to
@@ -195,6 +198,7 @@ struct tri_session {
   std::vector<TraceRec> trace;
   MetaLayout mlay[2];                          // layout of each metadata set as last staged
   hipEvent_t meta_ev[2] = {nullptr, nullptr};  // recorded after each metadata upload
+  int awork_n[2] = {0, 0};                     // entries of each set's compacted attention grid
   bool meta_pending[2] = {false, false};
   int prof_class = -1;
   std::vector<hipEvent_t> ev;  // start/stop pairs
@@ -334,6 +338,14 @@ int stage_meta(tri_session* s, int which, const HostRows& R, const std::vector<i
     memcpy(h.sidx, sidx.data(), sidx.size() * 4);
     memcpy(h.didx, didx.data(), didx.size() * 4);
   }
+  // the attention's compacted grid (bf16 attention only; 0 = regular grid)
+  int max_hi = 0;
+  for (int32_t v : R.hi) max_hi = std::max(max_hi, (int)v);
+  const tri_model_desc& d = s->m->d;
+  s->awork_n[which] = d.dtype == TRI_BF16
+                          ? attn_work_table(R.seq_start.data(), (int)R.slot_seq.size(), d.n_q_heads, d.n_kv_heads,
+                                            max_hi, h.awork, ML.awork_cap)
+                          : 0;
   return TRI_OK;
 }
 
@@ -418,6 +430,10 @@ int forward(tri_session* s, int which, const HostRows& R, float* logits_out) {
         while (a.kv_split < 4096 && a.kv_split < max_hi) a.kv_split *= 2;
       a.out = s->abuf;
       a.part = static_cast<float*>(s->attn_ws);
+      if (s->awork_n[which] > 0) {
+        a.work = dm.awork;
+        a.nwork = s->awork_n[which];
+      }
       a.v_f16 = dt == TRI_BF16;
       if (R.blk_len > 0) {
         a.row_blk = dm.blk;

@@ -178,10 +178,18 @@ struct AttnLaunch {
   const void* k_scr = nullptr;
   const void* v_scr = nullptr;
   int blk_len = 0;
+  // Compacted grid from attn_work_table (NULL: the regular grid).
+  const int32_t* work = nullptr;
+  int nwork = 0;
 };
 int attn_pick_split(int max_ctx, int n_seq, int hq, int hkv);
 int attn_pick_split_launch(int max_hi, int n_seq, int rows_per_seq, int hq, int hkv);
 size_t attn_ws_bytes(int rows, int hq, int hd, int max_hi, int kv_split);
+// Entries of the compacted attention grid of a forward whose slots start at
+// seq_start[0..n_slots] (host); 0 = launch the regular grid.
+int attn_work_table(const int32_t* seq_start, int n_slots, int hq, int hkv, int max_hi, int32_t* out, int cap);
+// Query vectors per query group of an attention launch (launch_attn's shape).
+int attn_group_vectors(int max_rows_per_seq, int G, int max_hi);
 hipError_t launch_attn(int dtype, const AttnLaunch& a, hipStream_t st);
 
 // Misc kernels.

@@ -10,6 +10,8 @@
 // Prints one line per check group and exits non-zero on a violation.
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
+#include <vector>
 
 #include "tri_common.h"
 
@@ -92,6 +94,46 @@ int main() {
       }
   }
   printf("attention: %ld split choices checked\n", splits);
+  // Compacted attention grid: for ragged slot layouts the table lists, slot
+  // by slot, exactly the query groups g with g * (group size) < the slot's
+  // query vectors (the groups the regular grid's workgroups find work in),
+  // and uniform layouts keep the regular grid (0 entries).
+  long tables = 0;
+  unsigned rng = 12345u;
+  auto next = [&](int mod) {
+    rng = rng * 1103515245u + 12345u;
+    return (int)((rng >> 8) % (unsigned)mod);
+  };
+  for (int trial = 0; trial < 4000; ++trial) {
+    const int hkv = 8, G = (int[]){1, 2, 4, 5, 8}[trial % 5], hq = G * hkv;
+    const int n = 2 + next(63), max_hi = (int[]){100, 600, 1600, 5000, 40000}[next(5)];
+    const bool uniform = trial % 7 == 0;
+    std::vector<int32_t> st(1, 0);
+    const int r0 = 1 + next(33);
+    for (int i = 0; i < n; ++i) st.push_back(st.back() + (uniform ? r0 : (next(4) == 0 ? 1 + next(64) : 1)));
+    int maxr = 0;
+    for (int i = 0; i < n; ++i) maxr = std::max(maxr, st[i + 1] - st[i]);
+    const int qv = attn_group_vectors(maxr, G, max_hi);
+    const int cap = st.back() + n;
+    std::vector<int32_t> out(cap, -1);
+    const int w = attn_work_table(st.data(), n, hq, hkv, max_hi, out.data(), cap);
+    std::vector<int32_t> want;
+    bool same = true;
+    const int g0 = ((st[1] - st[0]) * G + qv - 1) / qv;
+    for (int i = 0; i < n; ++i) {
+      const int groups = ((st[i + 1] - st[i]) * G + qv - 1) / qv;
+      same = same && groups == g0;
+      for (int g = 0; g * qv < (st[i + 1] - st[i]) * G; ++g) want.push_back(i * 65536 + g);
+    }
+    ++tables;
+    const bool ok = same ? w == 0 : (w == (int)want.size() && std::equal(want.begin(), want.end(), out.begin()));
+    if (!ok || qv % 32 || qv < 32 || qv > 128) {
+      printf("attention work table: trial %d, %d slots, G %d, max_hi %d: %d entries, expected %zu%s\n", trial, n, G,
+             max_hi, w, same ? (size_t)0 : want.size(), same ? " (uniform)" : "");
+      ++bad;
+    }
+  }
+  printf("attention work tables: %ld layouts checked\n", tables);
   printf(bad ? "FAIL %d\n" : "OK\n", bad);
   return bad ? 1 : 0;
 }

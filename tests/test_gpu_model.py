@@ -329,6 +329,44 @@ def test_small_bf16_rows_bit_identical_alone_and_in_a_wide_batch():
             assert np.array_equal(rec["logits"][rows], solo["logits"]), (f, i)
 
 
+def test_small_bf16_ragged_mixed_step_rows_bit_identical_alone():
+    """The attention's compacted grid (one workgroup per query group that
+    holds rows, for steps whose sequences carry different row counts): six
+    sequences stepped together in mixed AR / self-speculation steps give, row
+    for row, the logits and tokens of each sequence stepped alone (one slot:
+    the regular grid)."""
+    import self_speculative_lm_amd as tm
+    shape = seeded.SMALL_BF16
+    _, _, model, _ = get(shape)
+    prompts = [seeded.prompt(18 + 7 * i, shape.vocab, stream=150 + i) for i in range(6)]
+    AR, SS = tm.TRI_AR, tm.TRI_SELFSPEC
+    sched = [[SS, AR, AR, SS, AR, AR], [AR, AR, SS, AR, AR, AR], [AR, SS, AR, AR, SS, SS]]
+    sessions = []
+    for _ in range(2):
+        sess = tm.Session(model, max_batch=6, max_ctx=200, max_rows=6 * 34)
+        for i, p in enumerate(prompts):
+            sess.prefill(i, p)
+        sess.set_trace(True)
+        sessions.append(sess)
+    together, alone = sessions
+    for modes in sched:
+        out_t, _ = together.decode_step_mixed(modes, 32)
+        for i in range(6):
+            out_a, _ = alone.decode_step_mixed([modes[i] if j == i else -1 for j in range(6)], 32)
+            assert (out_a[i] == out_t[i]).all(), (modes, i)
+    tr_t, tr_a = together.trace(), alone.trace()
+    assert len(tr_a) == 6 * len(tr_t)
+    for f, rec in enumerate(tr_t):
+        step, which = divmod(f, 2)
+        for i in range(6):
+            solo = tr_a[(step * 6 + i) * 2 + which]
+            rows = rec["seq"] == i
+            assert (solo["seq"] == i).all()
+            for key in ("tok", "pos", "hi"):
+                assert (rec[key][rows] == solo[key]).all()
+            assert np.array_equal(rec["logits"][rows], solo["logits"]), (f, i)
+
+
 def test_small_bf16_1500_rows_bit_identical_to_50_row_chunks():
     """Batch invariance where the large-M GEMM keeps one slot for several K
     splits (the down projection's two splits chained in split order, at

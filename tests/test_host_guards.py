@@ -8,7 +8,9 @@
   workgroups;
 * the runtime's host code built with AddressSanitizer and
   UndefinedBehaviorSanitizer passes the host-only C-ABI tests (argument
-  validation, model and session sizing, the mode choice by concurrency)."""
+  validation, model and session sizing, the mode choice by concurrency) and
+  the launch-plan checks above (including the attention's compacted-grid
+  tables)."""
 import os
 import shutil
 import subprocess
@@ -61,4 +63,17 @@ def test_host_code_under_address_and_undefined_behaviour_sanitizers(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
     print(r.stdout[-2000:])
     assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
+    assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr, r.stderr[-4000:]
+    # the launch-plan checks (GEMM plans and reaches, attention splits and
+    # compacted-grid tables) against the sanitized host code as well
+    from self_speculative_lm_amd.build import hipcc
+    exe = str(tmp_path / "plan_bounds_san")
+    cmd = [hipcc(), "-O1", "-std=c++17", "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(PKG, "csrc"),
+           os.path.join(ROOT, "tests", "plan_bounds.cpp"), "-o", exe, "-L" + os.path.dirname(out),
+           "-l:" + os.path.basename(out), "-Wl,-rpath," + os.path.dirname(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, env=env)
+    print(r.stdout[-1000:])
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK"), r.stdout[-4000:] + r.stderr[-4000:]
     assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr, r.stderr[-4000:]
